@@ -1,0 +1,78 @@
+"""Pure-Python (no numpy arithmetic) paged decode, for tiny inputs only.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``).  Written independently of
+``paged.decode``: scalar loops, explicit index arithmetic into the flat
+storage of the pools, ``math.exp``.  It is the brute-force check that pins
+the vectorised oracle.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _bf16_to_float(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def decode_bruteforce(q, k_flat, v_flat, k_scale_flat, v_scale_flat, kv_dtype: str, Hkv: int, bs: int, D: int,
+                      block_tables, context_lens, scale: float):
+    """Same result as ``paged.decode`` from flat Python lists of the pools.
+
+    ``q`` is a nested list ``[B][Hq][D]`` of floats; ``k_flat``/``v_flat`` are
+    the pools flattened in storage order (ints for bf16 bit patterns and
+    int8 codes, floats for fp32); scales likewise (floats) or None.
+    """
+    x = {"f32": 4, "bf16": 2, "i8": 1}[kv_dtype]
+    x = 16 // x
+    B = len(q)
+    Hq = len(q[0])
+    G = Hq // Hkv
+
+    def load(flat, idx):
+        raw = flat[idx]
+        if kv_dtype == "bf16":
+            return _bf16_to_float(raw)
+        return float(raw)
+
+    def k_at(pb, h, t, d):
+        # K pool [nb][Hkv][D/x][bs][x]
+        idx = (((pb * Hkv + h) * (D // x) + d // x) * bs + t) * x + d % x
+        val = load(k_flat, idx)
+        if kv_dtype == "i8":
+            val *= float(k_scale_flat[(pb * Hkv + h) * bs + t])
+        return val
+
+    def v_at(pb, h, t, d):
+        # V pool [nb][Hkv][bs/x][D][x]
+        idx = (((pb * Hkv + h) * (bs // x) + t // x) * D + d) * x + t % x
+        val = load(v_flat, idx)
+        if kv_dtype == "i8":
+            val *= float(v_scale_flat[(pb * Hkv + h) * bs + t])
+        return val
+
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        L = int(context_lens[b])
+        for h in range(Hq):
+            kv = h // G
+            logits = []
+            for t in range(L):
+                pb = int(block_tables[b][t // bs])
+                off = t % bs
+                acc = 0.0
+                for d in range(D):
+                    acc += q[b][h][d] * k_at(pb, kv, off, d)
+                logits.append(scale * acc)
+            if L == 0:
+                continue
+            mx = max(logits)
+            weights = [math.exp(s - mx) for s in logits]
+            total = sum(weights)
+            for d in range(D):
+                num = 0.0
+                for t in range(L):
+                    pb = int(block_tables[b][t // bs])
+                    num += weights[t] * v_at(pb, kv, t % bs, d)
+                out[b][h][d] = num / total
+    return out
