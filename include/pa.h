@@ -1,0 +1,189 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention decode library.
+ *
+ * One new query token per sequence attends over that sequence's KV cache.
+ * The cache is a pool of fixed-size physical blocks shared by all
+ * sequences; sequence b reaches its tokens through row b of a block table
+ * (logical block j of the sequence lives in physical block
+ * block_tables[b][j]).  Sources: page "字节跳动 AI Infra (2)", question on
+ * vLLM and PagedAttention (block pool of 16-token blocks, per-request block
+ * tables, beams sharing prefix blocks with a copy-on-write last block, and
+ * the kernel sketch that turns a block-table entry into a K/V address);
+ * page "LLM推理优化", section 3.2 (fixed-size blocks, logical-to-physical
+ * mapping, copy-on-write sharing).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument except `cache` and `stream` is a DEVICE pointer
+ *   (HBM of the GPU that is current when the call is made).  `cache` is a
+ *   host pointer to a descriptor holding device pointers.
+ * - The caller owns all memory.  The library allocates nothing, frees
+ *   nothing, copies nothing to the host and never synchronises; it keeps no
+ *   state except a thread-local copy of the last HIP error.
+ * - Every call validates its host-visible arguments, then enqueues its
+ *   kernels on `stream` and returns.  PA_OK means "valid and launched", not
+ *   "finished".  On an error status nothing is launched and no output is
+ *   touched.
+ * - Device-resident values (context_lens, block-table entries, slots) are
+ *   not visible to the host and are not validated; the preconditions are
+ *   stated per call.  Kernels clamp out-of-range block ids and skip
+ *   out-of-range slots so that bad device data gives wrong numbers, never an
+ *   out-of-bounds access.
+ * - Reduction order depends only on logical positions, never on physical
+ *   block ids, and no floating-point atomics are used: results are bitwise
+ *   reproducible run to run and invariant under relabelling of blocks.
+ *
+ * Cache layout (x = elements per 16 bytes: fp32 4, bf16 8, int8 16)
+ * -----------------------------------------------------------------
+ *   k_cache  [num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *   v_cache  [num_blocks][num_kv_heads][block_size / x][head_dim][x]
+ *   k_scale, v_scale (int8 caches only): fp16 [num_blocks][num_kv_heads][block_size]
+ * Each (block, kv head) owns block_size * head_dim contiguous elements of
+ * each pool, so with one kv head block pb starts at element
+ * pb * block_size * head_dim, the address the pages' kernel sketch forms.
+ * Inside a block, K is stored in 16-byte channel groups per token and V in
+ * 16-byte token groups per channel, so that each lane of a wavefront loads
+ * exactly the 16 bytes its matrix-core operand needs.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_PTR = 1,      /* a required pointer is NULL (or a forbidden one is not) */
+  PA_ERR_BAD_SHAPE = 2,     /* a size is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = 3,   /* a valid but unimplemented combination (dtype, head_dim, block_size) */
+  PA_ERR_MISALIGNED = 4,    /* a pointer breaks the stated alignment */
+  PA_ERR_BAD_WORKSPACE = 5, /* split scratch too small for the call */
+  PA_ERR_HIP = 6            /* the HIP launch failed; see pa_last_hip_error() */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+
+/* Descriptor of one paged KV cache (one layer).  Pointers are device pointers. */
+typedef struct pa_kv_cache {
+  void *k_cache;        /* see layout above; 16-byte aligned */
+  void *v_cache;        /* see layout above; 16-byte aligned */
+  void *k_scale;        /* fp16, int8 caches only (else NULL); 16-byte aligned */
+  void *v_scale;        /* fp16, int8 caches only (else NULL); 16-byte aligned */
+  int32_t num_blocks;   /* blocks in the pool, >= 1 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t block_size;   /* tokens per block: 16, 32 or 64 */
+  int32_t head_dim;     /* 64 or 128 */
+  pa_dtype kv_dtype;    /* PA_F32, PA_BF16 or PA_I8 */
+} pa_kv_cache;
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into their cache slots.
+ *
+ * The cache grows by one row per token before attention reads it (page
+ * "字节跳动 AI Infra (2)", KV-cache question, step-t equations: the new K/V
+ * row is concatenated onto the cached ones).  Token i goes to slot
+ * s = slot_mapping[i]: physical block s / block_size, offset
+ * s % block_size; s < 0 (conventionally -1) skips the token.
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim], src_dtype, 16-byte aligned
+ *   slot_mapping  int32 [num_tokens], 4-byte aligned
+ *   src_dtype     PA_F32 for an fp32 cache; PA_BF16 for bf16 and int8 caches
+ *
+ * fp32/bf16 caches store the source bits unchanged.  int8 caches (INT8
+ * KV-cache quantisation: page "字节跳动 AI Infra (2)", optimisation table;
+ * page "LLM推理优化", section 1.3) store per (token, kv head) the fp16 scale
+ * s = fp16_rne(fp32(max|x| / 127)) and codes rint_even(fp32(x / s))
+ * clamped to [-127, 127] (all codes 0 when s is 0).  Bit-exact.
+ * Preconditions (device data): slots of one call are distinct; slots
+ * >= num_blocks * block_size are skipped.  num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                               int32_t num_tokens, const pa_kv_cache *cache, hipStream_t stream);
+
+/*
+ * pa_decode -- single-pass paged decode attention.
+ *
+ * For sequence b with L = context_lens[b] cached tokens (the newest one
+ * included) and query head h, with kv head kv = h / (num_heads /
+ * num_kv_heads) (consecutive query heads share one K/V head: GQA, MQA when
+ * num_kv_heads == 1; page "LLM推理优化", section 1.3):
+ *     out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t,   t < L,
+ * where token t lives in block block_tables[b][t / block_size] at offset
+ * t % block_size (page "字节跳动 AI Infra (2)", KV-cache question step-t
+ * equations and PagedAttention kernel sketch).  L == 0 gives a zero row.
+ *
+ *   q             [num_seqs][num_heads][head_dim], q_dtype, 16-byte aligned
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(L / block_size) are never read (may hold anything)
+ *   context_lens  int32 [num_seqs]
+ *   out           [num_seqs][num_heads][head_dim], out_dtype, 16-byte aligned
+ *   (q, kv, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16|F32),
+ *                        (BF16, I8, BF16|F32)
+ * Accumulation is fp32; bf16 outputs are the round-to-nearest-even of the
+ * fp32 result.  Tokens at positions >= L of the last block are never used,
+ * whatever they hold (NaN included).
+ * Preconditions (device data): 0 <= L <= max_blocks_per_seq * block_size;
+ * the first ceil(L / block_size) entries of each row are < num_blocks.
+ * num_seqs == 0 is a no-op.
+ */
+pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads, const pa_kv_cache *cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens, float scale,
+                    void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_decode_split -- first pass of KV-split decode (FlashDecoding: split
+ * along the KV length for long sequences; page "字节跳动 AI Infra (2)",
+ * third question, layer-2 table).
+ *
+ * Partition p of sequence b covers positions [p * partition_size,
+ * min((p + 1) * partition_size, L)).  For each (b, h, p) it writes the
+ * normalised partial output o_p = softmax restricted to that range applied
+ * to V, and lse_p = natural log of sum over the range of exp(scale * q.k_t).
+ * Partitions with no tokens get o_p = 0 and lse_p = -inf.
+ *
+ *   arguments up to `scale` as for pa_decode, then
+ *   partition_size      tokens per partition, a positive multiple of block_size
+ *   max_num_partitions  Pmax >= ceil(max_blocks_per_seq * block_size / partition_size)
+ *   part_out            fp32 [num_seqs][num_heads][Pmax][head_dim], 16-byte aligned
+ *   part_lse            fp32 [num_seqs][num_heads][Pmax], 4-byte aligned
+ * Every (b, h, p < Pmax) entry is written.
+ */
+pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                          const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, float scale, int32_t partition_size,
+                          int32_t max_num_partitions, float *part_out, float *part_lse, hipStream_t stream);
+
+/*
+ * pa_reduce -- second pass of KV-split decode: log-sum-exp merge.
+ *
+ * With n = ceil(L / partition_size) used partitions, M = max_p lse_p and
+ * w_p = exp(lse_p - M):  out[b][h] = sum_p w_p o_p / sum_p w_p  (online
+ * softmax statistics combine this way; page "LLM推理优化", section 2).
+ * L == 0 gives a zero row.  Arguments mirror pa_decode_split's; out as for
+ * pa_decode (out_dtype PA_F32 or PA_BF16).
+ */
+pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
+                    int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
+                    int32_t partition_size, void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/* Bytes of part_out plus part_lse for pa_decode_split (lse placed at a
+ * 256-byte aligned offset after part_out).  0 on invalid sizes. */
+size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions);
+
+/* Static, NUL-terminated description of a status code. */
+const char *pa_status_string(pa_status status);
+
+/* hipError_t value behind the calling thread's last PA_ERR_HIP (0 if none). */
+int32_t pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

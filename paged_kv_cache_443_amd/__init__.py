@@ -1,0 +1,202 @@
+"""Paged-attention decode for AMD MI355X (gfx950): Python binding.
+
+Thin marshalling layer over the C ABI of ``libpa.so`` (include/pa.h): each
+function takes torch tensors, checks that they are contiguous device
+tensors of the expected dtypes and shapes, and passes raw pointers, sizes
+and the current HIP stream to the library entry point of the same name.
+All computation happens in the library's HIP kernels; there is no CPU or
+PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PA_BF16, PA_F32, PA_I8, PaKvCache
+
+__all__ = [
+    "PAError",
+    "KVCache",
+    "reshape_and_cache",
+    "decode",
+    "decode_split",
+    "reduce",
+    "split_workspace_bytes",
+    "max_partitions",
+]
+
+_DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+_KV_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+_ELEM = {"f32": 4, "bf16": 2, "i8": 1}
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.status_string(status)
+        if status == _lib.PA_ERR_HIP:
+            msg += f" (hipError {_lib.lib().pa_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+
+
+def _check(fn: str, st: int) -> None:
+    if st != _lib.PA_OK:
+        raise PAError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclass
+class KVCache:
+    """One layer's paged KV cache: the two block pools (+ int8 scales).
+
+    Shapes (x = elements per 16 bytes):
+      k_cache [num_blocks, Hkv, head_dim // x, block_size, x]
+      v_cache [num_blocks, Hkv, block_size // x, head_dim, x]
+      k_scale, v_scale (int8 only): float16 [num_blocks, Hkv, block_size]
+    """
+
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]
+    v_scale: Optional[torch.Tensor]
+    num_blocks: int
+    num_kv_heads: int
+    block_size: int
+    head_dim: int
+    kv_dtype: str  # "f32" | "bf16" | "i8"
+
+    @property
+    def x(self) -> int:
+        return 16 // _ELEM[self.kv_dtype]
+
+    @staticmethod
+    def shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str):
+        x = 16 // _ELEM[kv_dtype]
+        return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+                (num_blocks, num_kv_heads, block_size // x, head_dim, x),
+                (num_blocks, num_kv_heads, block_size))
+
+    @classmethod
+    def allocate(cls, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str,
+                 device="cuda") -> "KVCache":
+        """Uninitialised pools (torch.empty) of the library's layout."""
+        ks, vs, ss = cls.shapes(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
+        dt = _KV_TORCH[kv_dtype]
+        k = torch.empty(ks, dtype=dt, device=device)
+        v = torch.empty(vs, dtype=dt, device=device)
+        sk = sv = None
+        if kv_dtype == "i8":
+            sk = torch.empty(ss, dtype=torch.float16, device=device)
+            sv = torch.empty(ss, dtype=torch.float16, device=device)
+        return cls(k, v, sk, sv, num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
+
+    def descriptor(self) -> PaKvCache:
+        ks, vs, ss = self.shapes(self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim, self.kv_dtype)
+        dt = _KV_TORCH[self.kv_dtype]
+        _need(self.k_cache, "k_cache", dt, ks)
+        _need(self.v_cache, "v_cache", dt, vs)
+        if self.kv_dtype == "i8":
+            _need(self.k_scale, "k_scale", torch.float16, ss)
+            _need(self.v_scale, "v_scale", torch.float16, ss)
+        return PaKvCache(_ptr(self.k_cache), _ptr(self.v_cache), _ptr(self.k_scale), _ptr(self.v_scale),
+                         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim,
+                         {"f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8}[self.kv_dtype])
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, cache: KVCache) -> None:
+    """Write tokens' K/V rows ``[T, Hkv, D]`` into slots ``slot_mapping[T]`` (int32, -1 skips)."""
+    T = key.shape[0]
+    src = torch.float32 if cache.kv_dtype == "f32" else torch.bfloat16
+    _need(key, "key", src, (T, cache.num_kv_heads, cache.head_dim))
+    _need(value, "value", src, (T, cache.num_kv_heads, cache.head_dim))
+    _need(slot_mapping, "slot_mapping", torch.int32, (T,))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_reshape_and_cache(_ptr(key), _ptr(value), _DT[src], _ptr(slot_mapping), T,
+                                         ctypes.byref(desc), _stream(key.device))
+    _check("pa_reshape_and_cache", st)
+
+
+def _decode_args(q, cache, block_tables, context_lens):
+    B, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("q head_dim differs from the cache's")
+    _need(q, "q", (torch.float32, torch.bfloat16))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    return B, Hq, D
+
+
+def decode(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           out: torch.Tensor) -> torch.Tensor:
+    """Single-pass paged decode attention; writes and returns ``out`` ``[B, Hq, D]``."""
+    B, Hq, D = _decode_args(q, cache, block_tables, context_lens)
+    _need(out, "out", (torch.float32, torch.bfloat16), (B, Hq, D))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_decode(_ptr(q), _DT[q.dtype], B, Hq, ctypes.byref(desc), _ptr(block_tables),
+                              block_tables.shape[1], _ptr(context_lens), float(scale), _ptr(out), _DT[out.dtype],
+                              _stream(q.device))
+    _check("pa_decode", st)
+    return out
+
+
+def max_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+    """Smallest max_num_partitions pa_decode_split accepts for a table width."""
+    return -(-(max_blocks_per_seq * block_size) // partition_size)
+
+
+def decode_split(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                 scale: float, partition_size: int, part_out: torch.Tensor, part_lse: torch.Tensor) -> None:
+    """KV-split first pass: ``part_out [B, Hq, Pmax, D]`` and ``part_lse [B, Hq, Pmax]`` (fp32)."""
+    B, Hq, D = _decode_args(q, cache, block_tables, context_lens)
+    if part_out.dim() != 4:
+        raise ValueError("part_out must be [num_seqs, num_heads, max_num_partitions, head_dim]")
+    Pmax = part_out.shape[2]
+    _need(part_out, "part_out", torch.float32, (B, Hq, Pmax, D))
+    _need(part_lse, "part_lse", torch.float32, (B, Hq, Pmax))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_decode_split(_ptr(q), _DT[q.dtype], B, Hq, ctypes.byref(desc), _ptr(block_tables),
+                                    block_tables.shape[1], _ptr(context_lens), float(scale), int(partition_size),
+                                    Pmax, _ptr(part_out), _ptr(part_lse), _stream(q.device))
+    _check("pa_decode_split", st)
+
+
+def reduce(part_out: torch.Tensor, part_lse: torch.Tensor, context_lens: torch.Tensor, partition_size: int,
+           out: torch.Tensor) -> torch.Tensor:
+    """KV-split second pass (log-sum-exp merge) into ``out`` ``[B, Hq, D]``."""
+    B, Hq, Pmax, D = part_out.shape
+    _need(part_out, "part_out", torch.float32)
+    _need(part_lse, "part_lse", torch.float32, (B, Hq, Pmax))
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(out, "out", (torch.float32, torch.bfloat16), (B, Hq, D))
+    st = _lib.lib().pa_reduce(_ptr(part_out), _ptr(part_lse), B, Hq, D, Pmax, _ptr(context_lens), int(partition_size),
+                              _ptr(out), _DT[out.dtype], _stream(out.device))
+    _check("pa_reduce", st)
+    return out
+
+
+def split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_num_partitions: int) -> int:
+    return int(_lib.lib().pa_split_workspace_bytes(num_seqs, num_heads, head_dim, max_num_partitions))

@@ -1,0 +1,162 @@
+// extern "C" entry points: validate, fill the kernel parameters, launch on
+// the caller's stream.  No allocation, no synchronisation.
+#include <cmath>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+#include "pa_validate.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+pa_status from_hip(hipError_t e) {
+  g_last_hip_error = static_cast<int32_t>(e);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+pa::DecodeParams make_decode_params(const void *q, int32_t num_seqs, int32_t num_heads, const pa_kv_cache *cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, float scale) {
+  pa::DecodeParams p{};
+  p.q = q;
+  p.k_cache = cache->k_cache;
+  p.v_cache = cache->v_cache;
+  p.k_scale = static_cast<const uint16_t *>(cache->k_scale);
+  p.v_scale = static_cast<const uint16_t *>(cache->v_scale);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.group = num_heads / cache->num_kv_heads;
+  p.head_groups = (p.group + 15) / 16;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = cache->num_blocks;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  return p;
+}
+
+pa_status launch(const pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stream) {
+  // one work-group per (kv head, query-head group, sequence[, partition])
+  const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
+  const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;
+  if (nwg > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  hipError_t e;
+  if (cache->kv_dtype == PA_F32)
+    e = pa::launch_decode_f32(p, cache->head_dim, cache->block_size, stream);
+  else
+    e = pa::launch_decode_mfma(p, cache->kv_dtype, cache->head_dim, cache->block_size, stream);
+  return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                               int32_t num_tokens, const pa_kv_cache *cache, hipStream_t stream) {
+  pa_status st = pa::check_append(key, value, src_dtype, slot_mapping, num_tokens, cache);
+  if (st != PA_OK || num_tokens == 0) return st;
+  if (static_cast<int64_t>(num_tokens) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  pa::AppendParams p{};
+  p.key = key;
+  p.value = value;
+  p.slot_mapping = slot_mapping;
+  p.k_cache = cache->k_cache;
+  p.v_cache = cache->v_cache;
+  p.k_scale = static_cast<uint16_t *>(cache->k_scale);
+  p.v_scale = static_cast<uint16_t *>(cache->v_scale);
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.block_size = cache->block_size;
+  p.head_dim = cache->head_dim;
+  p.num_blocks = cache->num_blocks;
+  return from_hip(pa::launch_append(p, cache->kv_dtype, stream));
+}
+
+pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads, const pa_kv_cache *cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens, float scale,
+                    void *out, pa_dtype out_dtype, hipStream_t stream) {
+  pa_status st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                                         context_lens, scale);
+  if (st != PA_OK || num_seqs == 0) return st;
+  st = pa::check_out(out, q_dtype, cache->kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  pa::DecodeParams p =
+      make_decode_params(q, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale);
+  p.out = out;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.partition_size = 0;
+  p.max_num_partitions = 1;
+  return launch(p, cache, stream);
+}
+
+pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                          const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, float scale, int32_t partition_size,
+                          int32_t max_num_partitions, float *part_out, float *part_lse, hipStream_t stream) {
+  pa_status st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                                         context_lens, scale);
+  if (st != PA_OK) return st;
+  st = pa::check_split(partition_size, max_num_partitions, cache->block_size, max_blocks_per_seq, part_out, part_lse);
+  if (st != PA_OK || num_seqs == 0) return st;
+  // partials are fp32; the dtype combination is that of an fp32-output decode
+  st = pa::check_out(part_out, q_dtype, cache->kv_dtype, PA_F32);
+  if (st != PA_OK) return st;
+  pa::DecodeParams p =
+      make_decode_params(q, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale);
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.partition_size = partition_size;
+  p.max_num_partitions = max_num_partitions;
+  return launch(p, cache, stream);
+}
+
+pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
+                    int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
+                    int32_t partition_size, void *out, pa_dtype out_dtype, hipStream_t stream) {
+  pa_status st = pa::check_reduce(part_out, part_lse, num_seqs, num_heads, head_dim, max_num_partitions,
+                                  context_lens, partition_size, out, out_dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (static_cast<int64_t>(num_seqs) * num_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  pa::ReduceParams p{};
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.head_dim = head_dim;
+  p.max_num_partitions = max_num_partitions;
+  p.partition_size = partition_size;
+  p.out_bf16 = out_dtype == PA_BF16;
+  return from_hip(pa::launch_reduce(p, stream));
+}
+
+size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
+  return pa::split_workspace_bytes(num_seqs, num_heads, head_dim, max_num_partitions);
+}
+
+const char *pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_PTR: return "a required pointer is null, or a pointer that must be null is not";
+    case PA_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or block_size combination";
+    case PA_ERR_MISALIGNED: return "a pointer is not aligned as required";
+    case PA_ERR_BAD_WORKSPACE: return "max_num_partitions too small for max_blocks_per_seq * block_size";
+    case PA_ERR_HIP: return "HIP kernel launch failed (see pa_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int32_t pa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Cache append: write each new token's K and V rows into its slot.
+//
+// The cache grows by one row per token before attention reads it (page
+// "字节跳动 AI Infra (2)", KV-cache question, step-t equations).  Slot s names
+// physical block s / block_size at offset s % block_size.  fp32 and bf16
+// caches take the source bits unchanged; int8 caches (INT8 KV cache: page
+// "字节跳动 AI Infra (2)", optimisation table; page "LLM推理优化", section 1.3)
+// take per (token, kv head) the fp16 scale fp16_rne(fp32(max|x| / 127)) and
+// codes rint_even(fp32(x / scale)) clamped to [-127, 127], all zero when the
+// scale is zero.  The divisions are IEEE fp32 (the compiler's default
+// correctly rounded division), so the result is bit-exact.
+//
+// One wavefront per (token, kv head); lane l owns channels PER*l .. PER*l+PER-1.
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Element offsets in the two pools (see the layout in pa.h).
+template <int D, int BS, int X>
+__device__ __forceinline__ size_t k_off(size_t tile, int o, int d) {
+  return ((tile * (D / X) + d / X) * BS + o) * X + d % X;
+}
+template <int D, int BS, int X>
+__device__ __forceinline__ size_t v_off(size_t tile, int o, int d) {
+  return ((tile * (BS / X) + o / X) * D + d) * X + o % X;
+}
+
+template <int KIND, int D, int BS>  // KIND: 0 fp32, 1 bf16, 2 int8
+__global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
+  constexpr int PER = D / 64;
+  constexpr int X = KIND == 0 ? 4 : (KIND == 1 ? 8 : 16);
+  const int lane = threadIdx.x;
+  const int id = blockIdx.x;
+  const int h = id % p.num_kv_heads;
+  const int i = id / p.num_kv_heads;
+  const int32_t slot = p.slot_mapping[i];
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(p.num_blocks) * BS) return;
+  const int pb = slot / BS;
+  const int o = slot % BS;
+  const size_t tile = static_cast<size_t>(pb) * p.num_kv_heads + h;
+  const size_t src = (static_cast<size_t>(i) * p.num_kv_heads + h) * D;
+
+  if constexpr (KIND == 0) {
+    const float *kk = static_cast<const float *>(p.key) + src;
+    const float *vv = static_cast<const float *>(p.value) + src;
+    float *kc = static_cast<float *>(p.k_cache);
+    float *vc = static_cast<float *>(p.v_cache);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = PER * lane + k;
+      kc[k_off<D, BS, X>(tile, o, d)] = kk[d];
+      vc[v_off<D, BS, X>(tile, o, d)] = vv[d];
+    }
+  } else if constexpr (KIND == 1) {
+    const uint16_t *kk = static_cast<const uint16_t *>(p.key) + src;
+    const uint16_t *vv = static_cast<const uint16_t *>(p.value) + src;
+    uint16_t *kc = static_cast<uint16_t *>(p.k_cache);
+    uint16_t *vc = static_cast<uint16_t *>(p.v_cache);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = PER * lane + k;
+      kc[k_off<D, BS, X>(tile, o, d)] = kk[d];
+      vc[v_off<D, BS, X>(tile, o, d)] = vv[d];
+    }
+  } else {
+    const uint16_t *src_rows[2] = {static_cast<const uint16_t *>(p.key) + src,
+                                   static_cast<const uint16_t *>(p.value) + src};
+    int8_t *pools[2] = {static_cast<int8_t *>(p.k_cache), static_cast<int8_t *>(p.v_cache)};
+    uint16_t *scales[2] = {p.k_scale, p.v_scale};
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float xv[PER];
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        xv[k] = bf16_bits_to_float(src_rows[which][PER * lane + k]);
+        amax = fmaxf(amax, fabsf(xv[k]));
+      }
+      amax = wave_max(amax);
+      const uint16_t s16 = float_to_half_bits(amax / 127.0f);
+      const float sf = half_bits_to_float(s16);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int d = PER * lane + k;
+        float qf = 0.f;
+        if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -127.f), 127.f);
+        const size_t off = which == 0 ? k_off<D, BS, X>(tile, o, d) : v_off<D, BS, X>(tile, o, d);
+        pools[which][off] = static_cast<int8_t>(static_cast<int>(qf));
+      }
+      if (lane == 0) scales[which][tile * BS + o] = s16;
+    }
+  }
+}
+
+template <int KIND, int D>
+hipError_t launch_bs(const AppendParams &p, hipStream_t s) {
+  const uint32_t nwg = static_cast<uint32_t>(static_cast<int64_t>(p.num_tokens) * p.num_kv_heads);
+  switch (p.block_size) {
+    case 16: hipLaunchKernelGGL((append_kernel<KIND, D, 16>), dim3(nwg), dim3(64), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((append_kernel<KIND, D, 32>), dim3(nwg), dim3(64), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((append_kernel<KIND, D, 64>), dim3(nwg), dim3(64), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_d(const AppendParams &p, hipStream_t s) {
+  if (p.head_dim == 128) return launch_bs<KIND, 128>(p, s);
+  if (p.head_dim == 64) return launch_bs<KIND, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s) {
+  switch (kv_dtype) {
+    case PA_F32: return launch_d<0>(p, s);
+    case PA_BF16: return launch_d<1>(p, s);
+    case PA_I8: return launch_d<2>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,458 @@
+// Paged decode attention on the CDNA4 matrix cores (bf16 and int8 KV caches).
+//
+// What is computed (page "字节跳动 AI Infra (2)", KV-cache question, step-t
+// equations): for each sequence and query head, softmax(scale * q . k_t)
+// over the cached tokens t < L, applied to the v_t; the tokens are found
+// through the block table (same page, PagedAttention kernel sketch), and
+// the query heads of one GQA group share a K/V head (page "LLM推理优化",
+// section 1.3).  The softmax is accumulated online, chunk by chunk, with
+// running max / sum statistics (page "LLM推理优化", section 2: tiles of K/V
+// are brought on chip, softmax statistics are updated per tile and the
+// output accumulated, so no full score vector is stored); the KV-split form
+// (FlashDecoding, page "字节跳动 AI Infra (2)", third question) writes per-
+// partition normalised outputs and log-sum-exps instead of the final row.
+//
+// Work decomposition.  One work-group (NW wavefronts) per (kv head, group of
+// <= 16 query heads, sequence[, partition]).  The wavefronts interleave over
+// chunks of CT consecutive tokens (32 for bf16, 64 for int8: 16 KiB of K+V
+// per chunk at head_dim 128), keep one chunk in flight while computing the
+// previous one, and merge their softmax states through LDS at the end.
+//
+// Matrix-core mapping (v_mfma_f32_16x16x32_bf16, wave64):
+//   S^T[token][head] = K[token][:] . Q[head][:]   A = 16 K rows, B = Q^T
+//   O^T[d][head]    += V^T[d][token] P^T[token][head]   A = V^T, B = P^T
+// The query heads of the GQA group are the N dimension, so one K/V tile
+// read from HBM serves all of them.  Lane (m = lane % 16, j = lane / 16):
+//   - QK, row group q: A row m is token TPL*(m/4) + 4q + (m%4); the output
+//     gives lane (j, head m) the scores of tokens TPL*j + 4q + i, i < 4;
+//   - PV: the B operand of lane (j, head m) is P of tokens TPL*j + 8r + e,
+//     exactly the scores that lane already holds, and the A operand of lane
+//     (j, channel m) is V of those 8 tokens at one channel: one 16-byte load
+//     in the token-grouped V layout.
+// K's channel-grouped layout makes each QK A-operand 16 contiguous bytes too.
+// P enters the matrix core as bf16 hi + lo parts (two products), so the
+// probabilities keep ~16 significant bits; scores and accumulators are fp32.
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+template <bool I8, int D>
+struct Tile {
+  static constexpr int X = I8 ? 16 : 8;      // elements per 16 bytes
+  static constexpr int TPL = I8 ? 16 : 8;    // tokens per lane group per chunk
+  static constexpr int CT = 4 * TPL;         // tokens per chunk
+  static constexpr int NQ = CT / 16;         // QK row groups per chunk
+  static constexpr int NS = D / 32;          // MFMA k-steps over head_dim
+  static constexpr int NKL = D / (4 * X);    // 16-byte K loads per lane per row group
+  static constexpr int ND = D / 16;          // 16-channel blocks of the output
+  static constexpr int NR = TPL / 8;         // PV products per channel block
+};
+
+// Registers one chunk occupies while its loads are in flight.
+template <bool I8, int D>
+struct KBuf {
+  u32x4 k[Tile<I8, D>::NQ][Tile<I8, D>::NKL];
+  u32x4 ks[I8 ? 2 : 1];  // int8: this lane group's 16 K scales
+};
+template <bool I8, int D>
+struct VBuf {
+  u32x4 v[Tile<I8, D>::ND];
+  u32x4 vs[I8 ? 2 : 1];  // int8: this lane group's 16 V scales
+};
+
+// Physical block ids this lane needs for one chunk (its K rows and its V tokens).
+struct Ids {
+  int32_t k, v;
+};
+
+template <bool I8, int D, int BS>
+struct Ctx {
+  const u32x4 *kpool;
+  const u32x4 *vpool;
+  const u32x4 *kscale;   // int8 only: fp16 scales viewed as 16-byte vectors
+  const u32x4 *vscale;
+  const int32_t *tbl;    // LDS copy of the block-table window
+  int32_t lb0;           // logical block of tbl[0]
+  int32_t nbv;           // logical blocks holding positions < t1
+  int32_t num_blocks_m1;
+  int32_t kvh;
+  int32_t hkv;
+  int32_t t1;
+  int32_t m, j;
+};
+
+// Block ids of chunk starting at position cs, read from the LDS table window.
+template <bool I8, int D, int BS>
+__device__ __forceinline__ Ids read_ids(const Ctx<I8, D, BS> &x, int cs) {
+  using T = Tile<I8, D>;
+  const int lbk = min((cs + T::TPL * (x.m >> 2)) / BS, x.nbv - 1) - x.lb0;
+  const int lbv = min((cs + T::TPL * x.j) / BS, x.nbv - 1) - x.lb0;
+  Ids r;
+  // out-of-range ids are clamped so that a bad table can never fault
+  r.k = static_cast<int32_t>(min(static_cast<uint32_t>(x.tbl[lbk]), static_cast<uint32_t>(x.num_blocks_m1)));
+  r.v = static_cast<int32_t>(min(static_cast<uint32_t>(x.tbl[lbv]), static_cast<uint32_t>(x.num_blocks_m1)));
+  return r;
+}
+
+template <bool I8, int D, int BS>
+__device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
+  using T = Tile<I8, D>;
+  const size_t ktile = static_cast<size_t>(static_cast<uint32_t>(id.k) * static_cast<uint32_t>(x.hkv) + x.kvh);
+  // K: [tile][D/X][BS] 16-byte vectors
+  const u32x4 *kp = x.kpool + ktile * (D / T::X) * BS;
+#pragma unroll
+  for (int q = 0; q < T::NQ; ++q) {
+    const int ok = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
+#pragma unroll
+    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = kp[(4 * s + x.j) * BS + ok];
+  }
+  if constexpr (I8) {
+    const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
+    const size_t sidx = (vtile * BS + (cs + T::TPL * x.j) % BS) / 8;
+    kb.ks[0] = x.kscale[sidx];
+    kb.ks[1] = x.kscale[sidx + 1];
+  }
+}
+
+template <bool I8, int D, int BS>
+__device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
+  using T = Tile<I8, D>;
+  const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
+  // V: [tile][BS/X][D] 16-byte vectors
+  const int ov = (cs + T::TPL * x.j) % BS;
+  const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) vb.v[n] = vp[16 * n];
+  if constexpr (I8) {
+    const size_t sidx = (vtile * BS + ov) / 8;
+    vb.vs[0] = x.vscale[sidx];
+    vb.vs[1] = x.vscale[sidx + 1];
+  }
+}
+
+template <bool I8, int D>
+struct Scores {
+  f32x4 s[Tile<I8, D>::NQ];  // row group q: tokens TPL*j + 4q + i of head m
+};
+template <bool I8, int D>
+struct Probs {
+  float p[Tile<I8, D>::NQ * 4];  // tokens TPL*j + e of head m
+};
+template <bool I8, int D>
+struct QOp {
+  bf16x8 q[Tile<I8, D>::NS];  // B operand of the QK product
+};
+
+template <bool I8, int D>
+struct State {
+  f32x4 acc[Tile<I8, D>::ND];  // O^T[16n + 4j + i][head m]
+  float m_run;                 // running max of log2-domain scores (head m)
+  float l_run;                 // this lane's share of the running sum
+};
+
+// Scores of one chunk: S^T = K Q^T (row group q holds tokens TPL*j + 4q + i).
+template <bool I8, int D>
+__device__ __forceinline__ void qk(Scores<I8, D> &S, const KBuf<I8, D> &kb, const QOp<I8, D> &qop) {
+  using T = Tile<I8, D>;
+#pragma unroll
+  for (int q = 0; q < T::NQ; ++q) {
+    S.s[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T::NS; ++s) {
+      bf16x8 a;
+      if constexpr (I8) {
+        const u32x4 w = kb.k[q][s >> 1];
+        a = (s & 1) ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = __builtin_bit_cast(bf16x8, kb.k[q][s]);
+      }
+      S.s[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop.q[s], S.s[q], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) { return half_bits_to_float(static_cast<uint16_t>(w & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return half_bits_to_float(static_cast<uint16_t>(w >> 16)); }
+
+// Online-softmax update for one chunk; returns the probabilities (V scale
+// folded in for int8) of this lane's tokens TPL*j + e.  TAIL: positions may
+// reach t1.
+template <bool I8, int D, bool TAIL>
+__device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, const KBuf<I8, D> &kb,
+                                        const VBuf<I8, D> &vb, Probs<I8, D> &P, int tok0, int t1, float scale_log2) {
+  using T = Tile<I8, D>;
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < T::NQ; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * q + i;
+      float sv;
+      if constexpr (I8) {
+        const uint32_t kw = kb.ks[e >> 3][(e >> 1) & 3];
+        sv = S.s[q][i] * (scale_log2 * ((e & 1) ? half_hi(kw) : half_lo(kw)));
+      } else {
+        sv = S.s[q][i] * scale_log2;
+      }
+      if constexpr (TAIL) sv = (tok0 + e < t1) ? sv : -INFINITY;
+      S.s[q][i] = sv;
+      mloc = fmaxf(mloc, sv);
+    }
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(st.m_run, mloc);
+  const float alpha = fast_exp2(st.m_run - m_new);
+  st.m_run = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int q = 0; q < T::NQ; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * q + i;
+      const float pe = fast_exp2(S.s[q][i] - m_new);
+      psum += pe;
+      if constexpr (I8) {
+        const uint32_t vw = vb.vs[e >> 3][(e >> 1) & 3];
+        float f = pe * ((e & 1) ? half_hi(vw) : half_lo(vw));  // V scale folded into P
+        if constexpr (TAIL) f = (tok0 + e < t1) ? f : 0.f;     // scale of an unused slot may be NaN
+        P.p[e] = f;
+      } else {
+        P.p[e] = pe;
+      }
+    }
+  }
+  st.l_run = st.l_run * alpha + psum;
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) st.acc[n] *= alpha;
+}
+
+// O^T += V^T P^T, P split into bf16 hi + lo parts.
+template <bool I8, int D, bool TAIL>
+__device__ __forceinline__ void pv_update(State<I8, D> &st, VBuf<I8, D> &vb, const Probs<I8, D> &P, int tok0,
+                                          int t1) {
+  using T = Tile<I8, D>;
+  if constexpr (TAIL && !I8) {
+    // V of positions >= t1 may hold NaN: zero it (0 * NaN would poison the sum)
+    uint32_t keep[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      keep[k] = ((tok0 + 2 * k < t1) ? 0x0000ffffu : 0u) | ((tok0 + 2 * k + 1 < t1) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int n = 0; n < T::ND; ++n)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vb.v[n][k] &= keep[k];
+  }
+#pragma unroll
+  for (int r = 0; r < T::NR; ++r) {
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = P.p[8 * r + e];
+      const __bf16 h = static_cast<__bf16>(f);
+      phi[e] = h;
+      plo[e] = static_cast<__bf16>(f - static_cast<float>(h));
+    }
+#pragma unroll
+    for (int n = 0; n < T::ND; ++n) {
+      bf16x8 a;
+      if constexpr (I8) {
+        const u32x4 w = vb.v[n];
+        a = r ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = __builtin_bit_cast(bf16x8, vb.v[n]);
+      }
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[n], 0, 0, 0);
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[n], 0, 0, 0);
+    }
+  }
+}
+
+constexpr int kTableWindow = 1024;  // block-table entries staged in LDS at a time
+
+template <bool I8, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
+  using T = Tile<I8, D>;
+  __shared__ float sm_acc[NW][16][D + 4];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ int32_t sm_tbl[kTableWindow];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int HX = p.num_kv_heads * p.head_groups;
+  const int id = blockIdx.x;
+  const int hx = id % HX;
+  const int rest = id / HX;
+  const int b = rest % p.num_seqs;
+  const int part = rest / p.num_seqs;
+  const int kvh = hx / p.head_groups;
+  const int g0 = (hx % p.head_groups) * 16;
+  const int gcount = min(16, p.group - g0);
+
+  Ctx<I8, D, BS> x;
+  x.m = lane & 15;
+  x.j = lane >> 4;
+  x.kvh = kvh;
+  x.hkv = p.num_kv_heads;
+  x.num_blocks_m1 = p.num_blocks - 1;
+  x.kpool = static_cast<const u32x4 *>(p.k_cache);
+  x.vpool = static_cast<const u32x4 *>(p.v_cache);
+  x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
+  x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
+  x.tbl = sm_tbl;
+  const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const int L = min(max(p.context_lens[b], 0), p.max_blocks_per_seq * BS);
+  int t0 = 0;
+  x.t1 = L;
+  if (p.partition_size > 0) {
+    t0 = part * p.partition_size;
+    x.t1 = min(t0 + p.partition_size, L);
+  }
+  x.nbv = (x.t1 + BS - 1) / BS;
+
+  // ---- query operand (B of the QK product): head m of the group -----------
+  QOp<I8, D> qop;
+  {
+    const bool qvalid = x.m < gcount;
+    const int hq = kvh * p.group + g0 + x.m;
+    const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(b) * p.num_heads + hq) * D;
+#pragma unroll
+    for (int s = 0; s < T::NS; ++s) {
+      const int d0 = I8 ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
+      qop.q[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  State<I8, D> st;
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+
+  // ---- token range in windows of staged block-table entries (usually one) ----
+  for (int ws = t0; ws < x.t1; ws += kTableWindow * BS) {
+    const int we = min(ws + kTableWindow * BS, x.t1);
+    x.lb0 = ws / BS;
+    const int nbw = (we + BS - 1) / BS - x.lb0;
+    __syncthreads();  // readers of the previous window are done
+    for (int i = threadIdx.x; i < nbw; i += NW * 64) sm_tbl[i] = table[x.lb0 + i];
+    __syncthreads();
+
+    // chunks ws + c*CT of this window; wave w takes c = w, w + NW, ...
+    const int nch = (we - ws + T::CT - 1) / T::CT;
+    const int n = w < nch ? (nch - w + NW - 1) / NW : 0;
+    if (n > 0) {
+      KBuf<I8, D> kb;
+      VBuf<I8, D> vb;
+      Scores<I8, D> S;
+      Probs<I8, D> P;
+      int cs = ws + w * T::CT;
+      Ids ids = read_ids(x, cs);
+      issue_k(kb, x, cs, ids);
+      issue_v(vb, x, cs, ids);
+      // steady state: K of the next chunk loads during this chunk's softmax and
+      // PV, V of the next chunk during the next chunk's QK
+      // (sched_barrier pins the load issue points: left alone, the scheduler
+      // sinks them next to their first use and nothing stays in flight)
+      for (int k = 0; k + 1 < n; ++k) {
+        const int cn = cs + NW * T::CT;
+        const Ids idn = read_ids(x, cn);
+        qk<I8, D>(S, kb, qop);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(kb, x, cn, idn);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax<I8, D, false>(st, S, kb, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
+        pv_update<I8, D, false>(st, vb, P, cs + T::TPL * x.j, x.t1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(vb, x, cn, idn);
+        __builtin_amdgcn_sched_barrier(0);
+        cs = cn;
+      }
+      // last chunk of this wave (the only one that can reach past t1)
+      qk<I8, D>(S, kb, qop);
+      softmax<I8, D, true>(st, S, kb, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
+      pv_update<I8, D, true>(st, vb, P, cs + T::TPL * x.j, x.t1);
+    }
+  }
+
+  // ---- merge the wavefronts' states -------------------------------------------
+  float l = st.l_run + __shfl_xor(st.l_run, 16);
+  l = l + __shfl_xor(l, 32);
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) *reinterpret_cast<f32x4 *>(&sm_acc[w][x.m][16 * n + 4 * x.j]) = st.acc[n];
+  if (x.j == 0) {
+    sm_m[w][x.m] = st.m_run;
+    sm_l[w][x.m] = l;
+  }
+  __syncthreads();
+
+  const bool split = p.partition_size > 0;
+  for (int e = threadIdx.x; e < gcount * D; e += NW * 64) {
+    const int gi = e / D;
+    const int d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v][gi]);
+    float o = 0.f;
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      float lsum = 0.f, osum = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float f = fast_exp2(sm_m[v][gi] - M);
+        lsum += f * sm_l[v][gi];
+        osum += f * sm_acc[v][gi][d];
+      }
+      o = osum / lsum;
+      lse = (M + __log2f(lsum)) * kLn2;
+    }
+    const int hq = kvh * p.group + g0 + gi;
+    const size_t row = static_cast<size_t>(b) * p.num_heads + hq;
+    if (split) {
+      const size_t prow = row * p.max_num_partitions + part;
+      p.part_out[prow * D + d] = o;
+      if (d == 0) p.part_lse[prow] = lse;
+    } else if (p.out_bf16) {
+      static_cast<uint16_t *>(p.out)[row * D + d] = float_to_bf16_bits(o);
+    } else {
+      static_cast<float *>(p.out)[row * D + d] = o;
+    }
+  }
+}
+
+template <bool I8, int D, int BS>
+hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
+  constexpr int NW = 4;
+  const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
+  const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool I8, int D>
+hipError_t launch_bs(const DecodeParams &p, int bs, hipStream_t s) {
+  switch (bs) {
+    case 16: return launch_t<I8, D, 16>(p, s);
+    case 32: return launch_t<I8, D, 32>(p, s);
+    case 64: return launch_t<I8, D, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s) {
+  const bool i8 = kv_dtype == PA_I8;
+  if (head_dim == 128) return i8 ? launch_bs<true, 128>(p, block_size, s) : launch_bs<false, 128>(p, block_size, s);
+  if (head_dim == 64) return i8 ? launch_bs<true, 64>(p, block_size, s) : launch_bs<false, 64>(p, block_size, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,73 @@
+// Internal interface between the C ABI layer (pa_api.cpp) and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Everything one decode launch needs, passed by value to the kernel.
+struct DecodeParams {
+  const void *q;              // [B][Hq][D]
+  const void *k_cache;        // K pool
+  const void *v_cache;        // V pool
+  const uint16_t *k_scale;    // fp16 bits, int8 caches only
+  const uint16_t *v_scale;    // fp16 bits, int8 caches only
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  void *out;                  // [B][Hq][D] (pa_decode)
+  float *part_out;            // [B][Hq][Pmax][D] (pa_decode_split)
+  float *part_lse;            // [B][Hq][Pmax]
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // num_heads / num_kv_heads
+  int32_t head_groups;        // ceil(group / 16): query-head groups of <= 16 per work-group
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t partition_size;     // 0: whole sequence (pa_decode)
+  int32_t max_num_partitions;
+  float scale;                // softmax scale as given
+  float scale_log2;           // scale * log2(e)
+  int32_t out_bf16;           // 1: bf16 output, 0: fp32 output
+};
+
+struct ReduceParams {
+  const float *part_out;
+  const float *part_lse;
+  const int32_t *context_lens;
+  void *out;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t max_num_partitions;
+  int32_t partition_size;
+  int32_t out_bf16;
+};
+
+struct AppendParams {
+  const void *key;
+  const void *value;
+  const int32_t *slot_mapping;
+  void *k_cache;
+  void *v_cache;
+  uint16_t *k_scale;
+  uint16_t *v_scale;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t num_blocks;
+};
+
+// Launchers (one per kernel family); each returns the launch's hipError_t.
+hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,108 @@
+// Host-side argument validation for the C ABI (no HIP calls).
+//
+// Checks run in a fixed order and the first failure is returned:
+// cache descriptor, sizes, the no-op case, pointers, dtypes, alignment.
+#include "pa_validate.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace pa {
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool supported_block_size(int32_t bs) { return bs == 16 || bs == 32 || bs == 64; }
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+pa_status check_cache(const pa_kv_cache *c) {
+  if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr) return PA_ERR_NULL_PTR;
+  if (c->kv_dtype != PA_F32 && c->kv_dtype != PA_BF16 && c->kv_dtype != PA_I8) return PA_ERR_UNSUPPORTED;
+  const bool want_scales = c->kv_dtype == PA_I8;
+  if (want_scales && (c->k_scale == nullptr || c->v_scale == nullptr)) return PA_ERR_NULL_PTR;
+  if (!want_scales && (c->k_scale != nullptr || c->v_scale != nullptr)) return PA_ERR_NULL_PTR;
+  if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1 || c->head_dim < 1) return PA_ERR_BAD_SHAPE;
+  if (!supported_block_size(c->block_size) || !supported_head_dim(c->head_dim)) return PA_ERR_UNSUPPORTED;
+  // block * kv-head tile indices are formed in 32 bits on the device
+  if (static_cast<int64_t>(c->num_blocks) * c->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  if (!aligned(c->k_cache, 16) || !aligned(c->v_cache, 16)) return PA_ERR_MISALIGNED;
+  if (want_scales && (!aligned(c->k_scale, 16) || !aligned(c->v_scale, 16))) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_append(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                       int32_t num_tokens, const pa_kv_cache *cache) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL_PTR;
+  const pa_dtype want = cache->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
+  if (src_dtype != want) return PA_ERR_UNSUPPORTED;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_decode_common(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                              const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, float scale) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_heads < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if (num_heads % cache->num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * cache->block_size > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_NULL_PTR;
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_out(const void *out, pa_dtype q_dtype, pa_dtype kv_dtype, pa_dtype out_dtype) {
+  if (out == nullptr) return PA_ERR_NULL_PTR;
+  const bool ok = (q_dtype == PA_F32 && kv_dtype == PA_F32 && out_dtype == PA_F32) ||
+                  (q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8) &&
+                   (out_dtype == PA_BF16 || out_dtype == PA_F32));
+  if (!ok) return PA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_split(int32_t partition_size, int32_t max_num_partitions, int32_t block_size,
+                      int32_t max_blocks_per_seq, const float *part_out, const float *part_lse) {
+  if (partition_size < 1 || partition_size % block_size != 0 || max_num_partitions < 1) return PA_ERR_BAD_SHAPE;
+  const int64_t max_len = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t need = (max_len + partition_size - 1) / partition_size;
+  if (max_num_partitions < need) return PA_ERR_BAD_WORKSPACE;
+  if (part_out == nullptr || part_lse == nullptr) return PA_ERR_NULL_PTR;
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
+                       int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
+                       int32_t partition_size, const void *out, pa_dtype out_dtype) {
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_num_partitions < 1 || partition_size < 1)
+    return PA_ERR_BAD_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (part_out == nullptr || part_lse == nullptr || context_lens == nullptr || out == nullptr)
+    return PA_ERR_NULL_PTR;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4) || !aligned(context_lens, 4) || !aligned(out, 16))
+    return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+size_t split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_num_partitions < 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * max_num_partitions;
+  const size_t out_bytes = rows * head_dim * sizeof(float);
+  const size_t lse_off = (out_bytes + 255) / 256 * 256;
+  return lse_off + rows * sizeof(float);
+}
+
+}  // namespace pa

@@ -1,0 +1,224 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_443_amd as pa
+from gpu_util import (DEV, TOL, bf16_rne_of, download_cache, fill_poison, gpu_append_tokens, max_err, meta,
+                      poisoned_cache, say, upload_oracle_cache)
+from workloads import make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_gpu(w, cache, out_dtype=torch.float32):
+    q, tables, lens = meta(w)
+    out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
+    pa.decode(q, cache, tables, lens, w.spec.scale, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _split_gpu(w, cache, P, out_dtype=torch.float32):
+    q, tables, lens = meta(w)
+    pmax = pa.max_partitions(tables.shape[1], w.spec.bs, P)
+    B, Hq, D = q.shape
+    po = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device=DEV)
+    pl = torch.empty((B, Hq, pmax), dtype=torch.float32, device=DEV)
+    pa.decode_split(q, cache, tables, lens, w.spec.scale, P, po, pl)
+    out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
+    pa.reduce(po, pl, lens, P, out)
+    torch.cuda.synchronize()
+    return po, pl, out, pmax
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_decode_matches_oracle(cfg):
+    w = make_workload(cfg, small=True)
+    say(f"[decode] cfg{cfg} small B={w.B} tokens={w.total_tokens()}")
+    oc = oracle.build_cache(w)
+    want = oracle.decode(w.q, oc, w.block_tables, w.context_lens, w.spec.scale)
+    cache = upload_oracle_cache(oc)
+    out = _decode_gpu(w, cache)
+    err = max_err(out, want)
+    say(f"  max abs err {err:.3e} (tol {TOL[w.spec.kv_dtype]})")
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert err <= TOL[w.spec.kv_dtype]
+    if w.spec.kv_dtype != "f32":
+        ob = _decode_gpu(w, cache, torch.bfloat16)
+        assert torch.equal(ob.view(torch.int16).cpu(), bf16_rne_of(out)), "bf16 out must be RNE of the fp32 out"
+
+
+@pytest.mark.parametrize("cfg,P", [(2, 512), (3, 256), (4, 512), (5, 1024), (1, 16)])
+def test_split_matches_oracle(cfg, P):
+    w = make_workload(cfg, small=True)
+    say(f"[split] cfg{cfg} P={P}")
+    oc = oracle.build_cache(w)
+    cache = upload_oracle_cache(oc)
+    po, pl, out, pmax = _split_gpu(w, cache, P)
+    want_po, want_pl = oracle.decode_partials(w.q, oc, w.block_tables, w.context_lens, w.spec.scale, P, pmax)
+    tol = TOL[w.spec.kv_dtype]
+    assert max_err(po, want_po) <= tol
+    gl = pl.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(want_pl)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.all(np.isneginf(gl[~fin]))
+    assert np.max(np.abs(gl[fin] - want_pl[fin])) <= 1e-3
+    want = oracle.decode(w.q, oc, w.block_tables, w.context_lens, w.spec.scale)
+    err = max_err(out, want)
+    say(f"  merged max abs err {err:.3e}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_append_bit_exact(cfg):
+    w = make_workload(cfg, small=True)
+    say(f"[append] cfg{cfg}")
+    cache = poisoned_cache(w)
+    gpu_append_tokens(w, cache)
+    torch.cuda.synchronize()
+    oc = oracle.build_cache(w)
+    k, v, ks, vs = download_cache(cache)
+    assert np.array_equal(k.view(np.uint8), oc.k.view(np.uint8))
+    assert np.array_equal(v.view(np.uint8), oc.v.view(np.uint8))
+    if w.spec.kv_dtype == "i8":
+        assert np.array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16))
+        assert np.array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16))
+
+
+def test_append_int8_edge_rows():
+    """Quantiser corner cases (ties, zero rows, subnormal scales, clamping) bit-exact."""
+    say("[append] int8 edge rows")
+    rng = np.random.default_rng(5)
+    D = 128
+    rows = [np.zeros(D), np.full(D, 2.0 ** -17 * 1.390625)]
+    base = np.array([127.0, 63.5, -1.0, 0.0, 62.5, -62.5, 0.5, -0.5] * 16)
+    rows += [base, base * 2.0 ** -20, -base * 3.0]
+    rows += [rng.standard_normal(D) * 10 ** rng.uniform(-6, 3) for _ in range(59)]
+    X = np.stack(rows).astype(np.float32)
+    from workloads import bf16_round
+    X = bf16_round(X)
+    T = X.shape[0]
+    K = X.reshape(T, 1, D)
+    V = -K
+    oc = oracle.PagedCache.empty("i8", 8, 1, 16, D)
+    slots = np.arange(T, dtype=np.int32) + 3
+    oracle.append(oc, K, V, slots)
+    c = pa.KVCache.allocate(8, 1, 16, D, "i8", DEV)
+    fill_poison(c)
+    from gpu_util import to_dev_values
+    pa.reshape_and_cache(to_dev_values(K, "bf16"), to_dev_values(V, "bf16"), torch.from_numpy(slots).to(DEV), c)
+    torch.cuda.synchronize()
+    k, v, ks, vs = download_cache(c)
+    assert np.array_equal(k, oc.k) and np.array_equal(v, oc.v)
+    assert np.array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16))
+    assert np.array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16))
+
+
+EDGE = []
+for kv in ("bf16", "i8", "f32"):
+    for bs in (16, 32, 64):
+        for D in (64, 128):
+            EDGE.append((kv, bs, D))
+
+
+@pytest.mark.parametrize("kv,bs,D", EDGE)
+def test_edge_lengths_and_groups(kv, bs, D):
+    """Lengths around block and chunk boundaries, empty sequences, several GQA groups."""
+    lens = [0, 1, bs - 1, bs, bs + 1, 31, 32, 33, 63, 64, 65, 129, 200]
+    for Hq, Hkv in ((8, 8), (8, 2), (16, 1), (32, 1), (12, 4)):
+        w = make_custom(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv, lengths=lens, seed=bs * D + Hq)
+        say(f"[edge] kv={kv} bs={bs} D={D} Hq={Hq} Hkv={Hkv}")
+        oc = oracle.build_cache(w)
+        want = oracle.decode(w.q, oc, w.block_tables, w.context_lens, w.spec.scale)
+        cache = upload_oracle_cache(oc)
+        out = _decode_gpu(w, cache)
+        assert max_err(out, want) <= TOL[kv], (Hq, Hkv)
+        assert torch.all(out[0] == 0)  # empty sequence
+        P = 2 * bs
+        po, pl, outs, pmax = _split_gpu(w, cache, P)
+        assert max_err(outs, want) <= TOL[kv], ("split", Hq, Hkv)
+
+
+def test_block_relabel_is_bitwise_invariant():
+    w = make_workload(3, small=True)
+    say("[relabel] cfg3 small")
+    oc = oracle.build_cache(w)
+    out1 = _decode_gpu(w, upload_oracle_cache(oc))
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(oc.num_blocks)
+    oc2 = oracle.PagedCache.empty(oc.kv_dtype, oc.num_blocks, oc.Hkv, oc.bs, oc.D)
+    oc2.k[perm] = oc.k
+    oc2.v[perm] = oc.v
+    w.block_tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    out2 = _decode_gpu(w, upload_oracle_cache(oc2))
+    assert torch.equal(out1, out2)
+
+
+def test_repeatable_bitwise():
+    w = make_workload(5, small=True)
+    say("[repeat] cfg5 small")
+    cache = upload_oracle_cache(oracle.build_cache(w))
+    a = _decode_gpu(w, cache)
+    b = _decode_gpu(w, cache)
+    assert torch.equal(a, b)
+    po1, pl1, o1, _ = _split_gpu(w, cache, 512)
+    po2, pl2, o2, _ = _split_gpu(w, cache, 512)
+    assert torch.equal(o1, o2) and torch.equal(pl1, pl2)
+
+
+def test_cow_beams_equal_bitwise():
+    """Beam pairs that share prefix blocks give identical rows for identical queries."""
+    w = make_workload(3, small=True)
+    say("[cow] cfg3 small")
+    oc = oracle.build_cache(w, include_last=False)
+    w.context_lens = np.maximum(w.context_lens - 1, 0).astype(np.int32)
+    for b2, a in w.pair_of.items():
+        w.q[b2] = w.q[a]
+    out = _decode_gpu(w, upload_oracle_cache(oc))
+    for b2, a in w.pair_of.items():
+        assert torch.equal(out[a], out[b2])
+
+
+def test_split_partition_sweep_agrees():
+    w = make_workload(4, small=True)
+    say("[sweep] cfg4 small partitions")
+    oc = oracle.build_cache(w)
+    want = oracle.decode(w.q, oc, w.block_tables, w.context_lens, w.spec.scale)
+    cache = upload_oracle_cache(oc)
+    for P in (64, 128, 512, 4096):
+        _, _, out, _ = _split_gpu(w, cache, P)
+        assert max_err(out, want) <= TOL["bf16"], P
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(cfg):
+    """Full-size workload, cache written by the GPU append, decode in the timed
+    launch configuration; sampled sequences checked against the oracle."""
+    w = make_workload(cfg)
+    s = w.spec
+    say(f"[full] cfg{cfg} B={w.B} tokens={w.total_tokens()} pool={w.num_blocks}")
+    cache = poisoned_cache(w)
+    gpu_append_tokens(w, cache, include_last=False)
+    Kn, Vn, sl = w.new_tokens()
+    src = "f32" if s.kv_dtype == "f32" else "bf16"
+    from gpu_util import to_dev_values
+    pa.reshape_and_cache(to_dev_values(Kn, src), to_dev_values(Vn, src), torch.from_numpy(sl).to(DEV), cache)
+    if s.partition_size:
+        _, _, out, _ = _split_gpu(w, cache, s.partition_size)
+    else:
+        out = _decode_gpu(w, cache)
+    assert torch.all(torch.isfinite(out))
+    rng = np.random.default_rng(cfg)
+    picks = sorted(set(rng.choice(w.B, size=min(3, w.B), replace=False).tolist()) | {int(np.argmax(w.context_lens))})
+    if w.pair_of:
+        b2, a = next(iter(w.pair_of.items()))
+        picks = sorted(set(picks) | {a, b2})
+    oc = oracle.build_cache(w, seqs=sorted(set(picks) | {w.pair_of[b] for b in picks if b in w.pair_of}))
+    want = oracle.decode(w.q[picks], oc, w.block_tables[picks], w.context_lens[picks], s.scale)
+    err = max_err(out[picks], want)
+    say(f"  sampled seqs {picks}: max abs err {err:.3e}")
+    assert err <= TOL[s.kv_dtype]
