@@ -53,15 +53,18 @@ struct Tile {
 };
 
 // Registers one chunk occupies while its loads are in flight.
+// K of the next chunk is loaded while this chunk's softmax still runs, so
+// everything the softmax reads besides the scores (the int8 scales) travels
+// with the V buffer, which stays live until the chunk is finished.
 template <bool I8, int D>
 struct KBuf {
   u32x4 k[Tile<I8, D>::NQ][Tile<I8, D>::NKL];
-  u32x4 ks[I8 ? 2 : 1];  // int8: this lane group's 16 K scales
 };
 template <bool I8, int D>
 struct VBuf {
-  u32x4 v[Tile<I8, D>::ND];
+  u32x4 ks[I8 ? 2 : 1];  // int8: this lane group's 16 K scales
   u32x4 vs[I8 ? 2 : 1];  // int8: this lane group's 16 V scales
+  u32x4 v[Tile<I8, D>::ND];
 };
 
 // Physical block ids this lane needs for one chunk (its K rows and its V tokens).
@@ -110,12 +113,6 @@ __device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x
 #pragma unroll
     for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = kp[(4 * s + x.j) * BS + ok];
   }
-  if constexpr (I8) {
-    const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
-    const size_t sidx = (vtile * BS + (cs + T::TPL * x.j) % BS) / 8;
-    kb.ks[0] = x.kscale[sidx];
-    kb.ks[1] = x.kscale[sidx + 1];
-  }
 }
 
 template <bool I8, int D, int BS>
@@ -124,14 +121,17 @@ __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x
   const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
   // V: [tile][BS/X][D] 16-byte vectors
   const int ov = (cs + T::TPL * x.j) % BS;
-  const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
-#pragma unroll
-  for (int n = 0; n < T::ND; ++n) vb.v[n] = vp[16 * n];
   if constexpr (I8) {
+    // scales first: the softmax needs them before PV needs the V data
     const size_t sidx = (vtile * BS + ov) / 8;
+    vb.ks[0] = x.kscale[sidx];
+    vb.ks[1] = x.kscale[sidx + 1];
     vb.vs[0] = x.vscale[sidx];
     vb.vs[1] = x.vscale[sidx + 1];
   }
+  const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) vb.v[n] = vp[16 * n];
 }
 
 template <bool I8, int D>
@@ -182,8 +182,8 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return half_bits_to_float
 // folded in for int8) of this lane's tokens TPL*j + e.  TAIL: positions may
 // reach t1.
 template <bool I8, int D, bool TAIL>
-__device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, const KBuf<I8, D> &kb,
-                                        const VBuf<I8, D> &vb, Probs<I8, D> &P, int tok0, int t1, float scale_log2) {
+__device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, const VBuf<I8, D> &vb, Probs<I8, D> &P,
+                                        int tok0, int t1, float scale_log2) {
   using T = Tile<I8, D>;
   float mloc = -INFINITY;
 #pragma unroll
@@ -193,7 +193,7 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
       const int e = 4 * q + i;
       float sv;
       if constexpr (I8) {
-        const uint32_t kw = kb.ks[e >> 3][(e >> 1) & 3];
+        const uint32_t kw = vb.ks[e >> 3][(e >> 1) & 3];
         sv = S.s[q][i] * (scale_log2 * ((e & 1) ? half_hi(kw) : half_lo(kw)));
       } else {
         sv = S.s[q][i] * scale_log2;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
         __builtin_amdgcn_sched_barrier(0);
         issue_k(kb, x, cn, idn);
         __builtin_amdgcn_sched_barrier(0);
-        softmax<I8, D, false>(st, S, kb, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
+        softmax<I8, D, false>(st, S, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
         pv_update<I8, D, false>(st, vb, P, cs + T::TPL * x.j, x.t1);
         __builtin_amdgcn_sched_barrier(0);
         issue_v(vb, x, cn, idn);
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
       }
       // last chunk of this wave (the only one that can reach past t1)
       qk<I8, D>(S, kb, qop);
-      softmax<I8, D, true>(st, S, kb, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
+      softmax<I8, D, true>(st, S, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
       pv_update<I8, D, true>(st, vb, P, cs + T::TPL * x.j, x.t1);
     }
   }
