@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+One step is one decode iteration of the whole path over a batch that is
+already resident in HBM: every sequence appends its newest K/V token to
+the paged cache (``pa_reshape_and_cache``), then attends over its cache
+(``pa_decode``, or ``pa_decode_split`` + ``pa_reduce`` for the long-context
+workload).  Before each timed step a 1 GiB read-modify-write of a scratch
+buffer evicts the L2s and the 256 MB Infinity Cache, so the K/V reads come
+from HBM.  Kernel times come from HIP events recorded on the stream the
+kernels run on (torch's current stream, which the binding launches on).
+
+Printed: ONE JSON line.  ``value`` is the effective HBM rate of a step:
+algorithmic bytes (K/V of every cached token -- prefix-shared blocks
+once -- int8 scales, q, out, used block-table entries, context lengths,
+and the appended rows) divided by the step's kernel time.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
+                  [--others 3,4,5] [--no-cpu-baseline]
+
+The ``cpu_baseline`` leg times the fp64 CPU oracle (the parity reference,
+not a tuned CPU implementation) on one host core over a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode attention µs/step + effective KV-read GB/s (% of HBM peak)"
+HEADLINE = 2
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5],
+                    help="workload timed for the headline value")
+    ap.add_argument("--others", default="3,4,5",
+                    help="comma-separated workloads also timed and summarised ('' for none)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="upper bound on the oracle's timed CPU work")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args(argv)
+
+
+# --------------------------------------------------------------------------
+# one workload on the GPU
+# --------------------------------------------------------------------------
+
+
+class Case:
+    """A workload resident on the GPU, with its step and its byte counts."""
+
+    def __init__(self, cfg: int, seed, torch, pa, perfmodel):
+        from workloads import make_workload
+        from workloads.device import append_tokens, meta, new_token_batch, poisoned_cache
+
+        self.torch = torch
+        self.pa = pa
+        t0 = time.time()
+        self.w = w = make_workload(cfg, seed)
+        s = self.s = w.spec
+        log(f"cfg{cfg} {s.name}: B={w.B} tokens={w.total_tokens()} pool={w.num_blocks} blocks; filling cache")
+        self.cache = poisoned_cache(w)
+        append_tokens(w, self.cache, include_last=False)
+        self.kn, self.vn, self.slots = new_token_batch(w)
+        self.q, self.tables, self.lens = meta(w)
+        self.out_dtype = torch.bfloat16 if s.q_dtype == "bf16" else torch.float32
+        self.out = torch.empty(self.q.shape, dtype=self.out_dtype, device=self.q.device)
+        self.split = s.partition_size is not None
+        if self.split:
+            self.pmax = pa.max_partitions(self.tables.shape[1], s.bs, s.partition_size)
+            B, Hq, D = self.q.shape
+            self.part_out = torch.empty((B, Hq, self.pmax, D), dtype=torch.float32, device=self.q.device)
+            self.part_lse = torch.empty((B, Hq, self.pmax), dtype=torch.float32, device=self.q.device)
+        torch.cuda.synchronize()
+        log(f"cfg{cfg}: cache filled in {time.time() - t0:.1f}s")
+
+        shared = sum(S * s.bs for S in w.shared_blocks.values())
+        kw = dict(Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs, kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
+                  out_dtype="bf16" if self.out_dtype == torch.bfloat16 else "f32")
+        self.decode_bytes = perfmodel.decode_bytes(w.context_lens, shared_tokens=shared, **kw)
+        self.decode_bytes_logical = perfmodel.decode_bytes(w.context_lens, **kw)
+        # the split pass reads everything the decode reads but writes partials, not out
+        self.split_kernel_bytes = self.decode_bytes - w.B * s.Hq * s.D * (2 if kw["out_dtype"] == "bf16" else 4)
+        n_new = int((self.slots.cpu() >= 0).sum())
+        self.append_bytes = perfmodel.append_bytes(n_new, Hkv=s.Hkv, D=s.D, kv_dtype=s.kv_dtype,
+                                                   src_dtype="f32" if s.kv_dtype == "f32" else "bf16")
+        self.step_bytes = self.decode_bytes + self.append_bytes
+        if self.split:
+            used = int(sum(-(-int(L) // s.partition_size) for L in w.context_lens))
+            self.scratch_bytes = perfmodel.split_scratch_bytes(w.B, s.Hq, s.D, used)
+        else:
+            self.scratch_bytes = 0
+
+    def step(self, ev=None):
+        """One decode step; ``ev`` = list of 4 events recorded between its launches."""
+        pa, s = self.pa, self.s
+        if ev:
+            ev[0].record()
+        pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
+        if ev:
+            ev[1].record()
+        if self.split:
+            pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
+                            self.part_out, self.part_lse)
+            if ev:
+                ev[2].record()
+            pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
+        else:
+            pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, self.out)
+            if ev:
+                ev[2].record()
+        if ev:
+            ev[3].record()
+
+    def decode_f32(self):
+        """The same decode into an fp32 output (parity check of the timed path)."""
+        torch, pa, s = self.torch, self.pa, self.s
+        out = torch.empty(self.q.shape, dtype=torch.float32, device=self.q.device)
+        if self.split:
+            pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
+                            self.part_out, self.part_lse)
+            pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, out)
+        else:
+            pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, out)
+        torch.cuda.synchronize()
+        return out
+
+    def free(self):
+        for name in ("cache", "q", "tables", "lens", "out", "part_out", "part_lse", "kn", "vn", "slots"):
+            if hasattr(self, name):
+                delattr(self, name)
+
+
+def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
+    torch = case.torch
+    for i in range(warmup):
+        flush.add_(1)
+        case.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.add_(1)  # evict L2 and Infinity Cache: the step's K/V reads come from HBM
+        case.step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda a, b: [evs[i][a].elapsed_time(evs[i][b]) for i in range(steps)]  # noqa: E731
+    app, dec, tail, step = ms(0, 1), ms(1, 2), ms(2, 3), ms(0, 3)
+
+    def stats(v):
+        v = sorted(v)
+        return {"mean_us": 1e3 * sum(v) / len(v), "median_us": 1e3 * v[len(v) // 2],
+                "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
+
+    r = {"append": stats(app), "decode_split" if case.split else "decode": stats(dec), "step": stats(step),
+         "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
+    if case.split:
+        r["reduce"] = stats(tail)
+    return r
+
+
+def summarise(case: Case, t: dict, peak: float) -> dict:
+    s = case.s
+    step_us = t["step"]["mean_us"]
+    key = "decode_split" if case.split else "decode"
+    dec_us = t[key]["mean_us"]
+    dec_bytes = case.split_kernel_bytes if case.split else case.decode_bytes
+    d = {
+        "workload": s.name,
+        "us_per_step": round(step_us, 2),
+        "step_GBps": round(case.step_bytes / step_us / 1e3, 1),
+        "step_frac_of_peak": round(case.step_bytes / step_us / 1e3 / peak, 4),
+        "kernel_us": {k: round(v["mean_us"], 2) for k, v in t.items() if isinstance(v, dict)},
+        "dominant_kernel": "pa_decode_split" if case.split else "pa_decode",
+        "dominant_GBps": round(dec_bytes / dec_us / 1e3, 1),
+        "dominant_frac_of_peak": round(dec_bytes / dec_us / 1e3 / peak, 4),
+        "bytes": {"step": case.step_bytes, "decode": case.decode_bytes,
+                  "decode_logical": case.decode_bytes_logical, "append": case.append_bytes,
+                  "split_scratch_overhead": case.scratch_bytes},
+    }
+    return d
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, one core, bounded sample
+# --------------------------------------------------------------------------
+
+
+def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32) -> dict:
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    w, s = case.w, case.s
+    host_cores = os.cpu_count()
+    allowed = sorted(os.sched_getaffinity(0))
+    log("cpu baseline: building the oracle's cache (not timed)")
+    oc = oracle.build_cache(w)
+    os.sched_setaffinity(0, {allowed[0]})
+    done, secs, toks, errs = [], 0.0, 0, []
+    try:
+        with threadpool_limits(limits=1):
+            for b in range(w.B):
+                sl = [b]
+                t0 = time.perf_counter()
+                want = oracle.decode(w.q[sl], oc, w.block_tables[sl], w.context_lens[sl], s.scale)
+                secs += time.perf_counter() - t0
+                done.append(b)
+                toks += int(w.context_lens[b])
+                errs.append(float(np.max(np.abs(gpu_out_f32[b].astype(np.float64) - want[0]))))
+                if secs >= budget_s:
+                    break
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    kw = dict(Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs, kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
+              out_dtype="bf16" if s.q_dtype == "bf16" else "f32")
+    sample_bytes = perfmodel.decode_bytes(w.context_lens[done], **kw)
+    return {
+        "value": round(sample_bytes / secs / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"oracle.decode (numpy fp64) over sequences 0..{done[-1]} of {w.B} ({toks} cached tokens, "
+                   f"{len(done)}/{w.B} of the batch) of the timed workload, one host core of {host_cores}"),
+        "seconds": round(secs, 2),
+        "us_per_step_equiv": round(secs * 1e6 * w.total_tokens() / max(toks, 1), 1),
+        "parity_max_abs_err_vs_gpu_fp32_out": max(errs) if errs else None,
+    }
+
+
+# --------------------------------------------------------------------------
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged-decode path has no "
+                                   "cross-GPU step here (see the sharding notes); run with --gpus 1"}),
+              flush=True)
+        return 2
+
+    log("importing torch")
+    import torch
+
+    import paged_kv_cache_443_amd as pa
+    from paged_kv_cache_443_amd import _lib, perfmodel
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    _lib.lib()  # fails loudly when the HIP library is not built
+    peak = perfmodel.HBM_PEAK_GBPS
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.zeros(args.flush_mib * (1 << 20) // 4, dtype=torch.int32, device=dev)
+
+    others = [int(c) for c in args.others.split(",") if c.strip()] if args.others else []
+    others = [c for c in others if c != args.config]
+
+    # headline workload
+    case = Case(args.config, args.seed, torch, pa, perfmodel)
+    log(f"timing cfg{args.config}: {args.warmup} warmup + {args.steps} steps")
+    t = time_case(case, args.steps, args.warmup, flush)
+    head = summarise(case, t, peak)
+    log(f"cfg{args.config}: {head['us_per_step']} us/step, {head['step_GBps']} GB/s "
+        f"({100 * head['step_frac_of_peak']:.1f}% of {peak:.0f}); dominant kernel "
+        f"{head['dominant_GBps']} GB/s")
+    out32 = case.decode_f32().cpu().numpy()
+
+    s = case.s
+    dec_key = "decode_split" if case.split else "decode"
+    dec_bytes = case.split_kernel_bytes if case.split else case.decode_bytes
+    dec_us = t[dec_key]["mean_us"]
+    roofline = {
+        "bound": "hbm",
+        "kernel": head["dominant_kernel"],
+        "achieved": round(dec_bytes / dec_us / 1e3, 1),
+        "peak": peak,
+        "unit": "GB/s",
+        "frac": round(dec_bytes / dec_us / 1e3 / peak, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": dec_bytes,
+        "avg_launch_us": round(dec_us, 2),
+    }
+
+    line = {
+        "metric": METRIC,
+        "value": head["step_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "us_per_step": head["us_per_step"],
+        "frac_of_hbm_peak": head["step_frac_of_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.kv_dtype if s.kv_dtype != "i8" else "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": s.name,
+            "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.D, "block_size": s.bs,
+            "kv_dtype": s.kv_dtype, "q_out_dtype": s.q_dtype, "cached_tokens": case.w.total_tokens(),
+            "partition_size": s.partition_size, "seed": case.w.seed,
+        },
+        "kernel_us": head["kernel_us"],
+        "bytes_per_step": head["bytes"],
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, perfmodel, out32)
+    case.free()
+    del case
+    torch.cuda.empty_cache()
+
+    other = {}
+    for c in others:
+        oc = Case(c, None, torch, pa, perfmodel)
+        log(f"timing cfg{c}")
+        ot = time_case(oc, args.steps, args.warmup, flush)
+        other[f"cfg{c}"] = summarise(oc, ot, peak)
+        log(f"cfg{c}: {other[f'cfg{c}']['us_per_step']} us/step, {other[f'cfg{c}']['step_GBps']} GB/s")
+        oc.free()
+        del oc
+        torch.cuda.empty_cache()
+    if other:
+        line["other_workloads"] = other
+
+    text = json.dumps(line)
+    print(text, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(text + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

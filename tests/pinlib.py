@@ -250,8 +250,33 @@ def check_bruteforce(decode: DecodeFn) -> None:
         _close(got, np.array(want), 1e-12, f"brute force {kv_dtype} bs{bs}")
 
 
+def check_dense_library(decode: DecodeFn) -> None:
+    """Against torch's CPU scaled_dot_product_attention (float64) on the
+    de-paged, contiguous K/V of each sequence: the textbook
+    softmax(q K^T * scale) V computed by a library routine, with K/V heads
+    repeated G times for GQA."""
+    import torch
+
+    rng = np.random.default_rng(23)
+    for Hq, Hkv, D, bs, lens in [(4, 4, 64, 16, (7, 16, 33, 40)), (8, 2, 32, 8, (1, 9, 30)),
+                                 (6, 1, 16, 4, (13, 5))]:
+        Ks = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+        Vs = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+        q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+        cache, tb, cl = paged_from_dense(Ks, Vs, bs, "f32", rng)
+        scale = 1.0 / math.sqrt(D)
+        got = decode(q, cache, tb, cl, scale)
+        G = Hq // Hkv
+        for b, L in enumerate(lens):
+            k = torch.from_numpy(Ks[b]).double().permute(1, 0, 2).repeat_interleave(G, dim=0)  # [Hq, L, D]
+            v = torch.from_numpy(Vs[b]).double().permute(1, 0, 2).repeat_interleave(G, dim=0)
+            qq = torch.from_numpy(q[b]).double().unsqueeze(1)  # [Hq, 1, D]
+            want = torch.nn.functional.scaled_dot_product_attention(qq, k, v, scale=scale)[:, 0].numpy()
+            _close(got[b], want, 1e-12, f"dense library Hq{Hq} Hkv{Hkv} seq{b}")
+
+
 ALL_DECODE_CHECKS = [check_closed_forms, check_shift_invariances, check_token_permutation, check_block_relabel,
-                     check_gqa_vs_mha, check_cow, check_bruteforce]
+                     check_gqa_vs_mha, check_cow, check_bruteforce, check_dense_library]
 
 
 # --------------------------------------------------------------------------
