@@ -5,9 +5,10 @@ One step is one decode iteration of the whole path over a batch that is
 already resident in HBM: every sequence appends its newest K/V token to
 the paged cache (``pa_reshape_and_cache``), then attends over its cache
 (``pa_decode``, or ``pa_decode_split`` + ``pa_reduce`` for the long-context
-workload).  Before each timed step a 1 GiB read-modify-write of a scratch
-buffer evicts the L2s and the 256 MB Infinity Cache, so the K/V reads come
-from HBM.  Kernel times come from HIP events recorded on the stream the
+workload).  Before each timed step a 1 GiB read of a scratch buffer evicts
+the L2s and the 256 MB Infinity Cache with clean lines, so the K/V reads
+come from HBM and no write-back of earlier data lands inside the timed
+kernels.  Kernel times come from HIP events recorded on the stream the
 kernels run on (torch's current stream, which the binding launches on).
 
 Printed: ONE JSON line.  ``value`` is the effective HBM rate of a step:
@@ -151,17 +152,29 @@ class Case:
                 delattr(self, name)
 
 
+class Flush:
+    """Evicts the L2s and the Infinity Cache by reading a 1 GiB buffer (a sum)."""
+
+    def __init__(self, torch, mib: int, device):
+        self.torch = torch
+        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.int32, device=device)
+        self.sink = torch.zeros((), dtype=torch.int64, device=device)
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=0, dtype=self.torch.int64, out=self.sink)
+
+
 def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
     torch = case.torch
     for i in range(warmup):
-        flush.add_(1)
+        flush()
         case.step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        flush.add_(1)  # evict L2 and Infinity Cache: the step's K/V reads come from HBM
+        flush()  # evict L2 and Infinity Cache: the step's K/V reads come from HBM
         case.step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -275,7 +288,7 @@ def main(argv=None) -> int:
     peak = perfmodel.HBM_PEAK_GBPS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    flush = torch.zeros(args.flush_mib * (1 << 20) // 4, dtype=torch.int32, device=dev)
+    flush = Flush(torch, args.flush_mib, dev)
 
     others = [int(c) for c in args.others.split(",") if c.strip()] if args.others else []
     others = [c for c in others if c != args.config]

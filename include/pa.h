@@ -38,12 +38,18 @@
  *   k_cache  [num_blocks][num_kv_heads][head_dim / x][block_size][x]
  *   v_cache  [num_blocks][num_kv_heads][block_size / x][head_dim][x]
  *   k_scale, v_scale (int8 caches only): fp16 [num_blocks][num_kv_heads][block_size]
+ * K of (block pb, kv head h, in-block offset t, channel d) is
+ * k_cache[pb][h][d / x][slot(t)][d % x] with slot(t) = t for fp32 and int8
+ * caches and, for bf16 caches, t with its bits 2 and 3 exchanged (offsets
+ * 0-3, 8-11, 4-7, 12-15 in every group of 16).  V of (pb, h, t, d) is
+ * v_cache[pb][h][t / x][d][t % x].  Scales are indexed by t.
  * Each (block, kv head) owns block_size * head_dim contiguous elements of
  * each pool, so with one kv head block pb starts at element
  * pb * block_size * head_dim, the address the pages' kernel sketch forms.
  * Inside a block, K is stored in 16-byte channel groups per token and V in
  * 16-byte token groups per channel, so that each lane of a wavefront loads
- * exactly the 16 bytes its matrix-core operand needs.
+ * exactly the 16 bytes its matrix-core operand needs; the bf16 slot order
+ * makes every K load instruction cover whole 128-byte lines.
  */
 #ifndef PA_H_
 #define PA_H_

@@ -36,8 +36,13 @@ def decode_bruteforce(q, k_flat, v_flat, k_scale_flat, v_scale_flat, kv_dtype: s
         return float(raw)
 
     def k_at(pb, h, t, d):
-        # K pool [nb][Hkv][D/x][bs][x]
-        idx = (((pb * Hkv + h) * (D // x) + d // x) * bs + t) * x + d % x
+        # K pool [nb][Hkv][D/x][bs][x]; bf16 tiles hold offset t at the slot
+        # whose bits 2 and 3 are those of t exchanged
+        slot = t
+        if kv_dtype == "bf16":
+            b2, b3 = (t >> 2) & 1, (t >> 3) & 1
+            slot = t - 4 * b2 - 8 * b3 + 8 * b2 + 4 * b3
+        idx = (((pb * Hkv + h) * (D // x) + d // x) * bs + slot) * x + d % x
         val = load(k_flat, idx)
         if kv_dtype == "i8":
             val *= float(k_scale_flat[(pb * Hkv + h) * bs + t])

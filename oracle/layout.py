@@ -7,7 +7,10 @@ sequences; a sequence reaches its blocks through its block table):
 
 * ``x`` = number of elements in 16 bytes (fp32: 4, bf16: 8, int8: 16);
 * K pool ``[num_blocks][Hkv][D/x][bs][x]``: K of (block pb, kv head h,
-  in-block offset t, channel d) is ``K[pb, h, d // x, t, d % x]``;
+  in-block offset t, channel d) is ``K[pb, h, d // x, slot(t), d % x]``,
+  where ``slot(t) = t`` for fp32 and int8 caches and, for bf16 caches,
+  ``t`` with bits 2 and 3 exchanged (inside every group of 16 offsets the
+  order is 0-3, 8-11, 4-7, 12-15);
 * V pool ``[num_blocks][Hkv][bs/x][D][x]``: V of (pb, h, t, d) is
   ``V[pb, h, t // x, d, t % x]``;
 * int8 only: fp16 scales ``[num_blocks][Hkv][bs]`` for K and for V.
@@ -33,6 +36,18 @@ _BF16_NAN = np.uint16(0x7FC0)
 
 def x_per_16b(kv_dtype: str) -> int:
     return 16 // _ELEM_BYTES[kv_dtype]
+
+
+def k_slot(offs, kv_dtype: str):
+    """Position inside a K tile's token axis of in-block offset(s) ``offs``.
+
+    Identity for fp32 and int8 caches; bf16 caches exchange bits 2 and 3 of
+    the offset.
+    """
+    if kv_dtype != "bf16":
+        return offs
+    o = np.asarray(offs)
+    return (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1)
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -92,7 +107,7 @@ class PagedCache:
     # ---- element access (float64) ---------------------------------------
     def k_rows(self, pbs: np.ndarray, h: int, offs: np.ndarray) -> np.ndarray:
         """K of tokens (pbs[i], offs[i]) of kv head h as float64 ``[n, D]``."""
-        raw = self.k[pbs, h, :, offs, :].reshape(len(pbs), self.D)  # [n, D/x, x] -> [n, D]
+        raw = self.k[pbs, h, :, k_slot(offs, self.kv_dtype), :].reshape(len(pbs), self.D)  # [n, D/x, x] -> [n, D]
         return self._to_f64(raw, self.k_scale, pbs, h, offs)
 
     def v_rows(self, pbs: np.ndarray, h: int, offs: np.ndarray) -> np.ndarray:
@@ -119,8 +134,8 @@ class PagedCache:
         hh = np.arange(H)[None, :]
         P = pbs[:, None]
         O = offs[:, None]
-        # K[pb, h, d//x, t, d%x]
-        self.k[P, hh, :, O, :] = kraw.reshape(n, H, self.D // x, x)
+        # K[pb, h, d//x, slot(t), d%x]
+        self.k[P, hh, :, k_slot(O, self.kv_dtype), :] = kraw.reshape(n, H, self.D // x, x)
         # V[pb, h, t//x, d, t%x]
         self.v[P, hh, O // x, :, O % x] = vraw
         if self.kv_dtype == "i8":

@@ -75,6 +75,8 @@ class KVCache:
       k_cache [num_blocks, Hkv, head_dim // x, block_size, x]
       v_cache [num_blocks, Hkv, block_size // x, head_dim, x]
       k_scale, v_scale (int8 only): float16 [num_blocks, Hkv, block_size]
+    bf16 K tiles keep in-block offset t at slot t with bits 2 and 3
+    exchanged; write them through ``reshape_and_cache``.
     """
 
     k_cache: torch.Tensor

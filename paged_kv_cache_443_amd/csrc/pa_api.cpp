@@ -1,5 +1,6 @@
 // extern "C" entry points: validate, fill the kernel parameters, launch on
 // the caller's stream.  No allocation, no synchronisation.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -43,7 +44,19 @@ pa::DecodeParams make_decode_params(const void *q, int32_t num_seqs, int32_t num
   return p;
 }
 
-pa_status launch(const pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stream) {
+// Block-table entries a work-group stages at once: the whole range its unit
+// can touch (the table row, or one partition), at most kMaxTableWindow.
+constexpr int32_t kMaxTableWindow = 1024;
+
+int32_t table_window(int32_t max_blocks_per_seq, int32_t partition_size, int32_t block_size) {
+  int32_t w = max_blocks_per_seq;
+  if (partition_size > 0) w = std::min(w, partition_size / block_size);
+  w = std::min(std::max(w, 1), kMaxTableWindow);
+  return (w + 3) / 4 * 4;
+}
+
+pa_status launch(pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stream) {
+  p.tbl_window = table_window(p.max_blocks_per_seq, p.partition_size, cache->block_size);
   // one work-group per (kv head, query-head group, sequence[, partition])
   const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;

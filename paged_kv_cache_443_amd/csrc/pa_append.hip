@@ -11,6 +11,8 @@
 // correctly rounded division), so the result is bit-exact.
 //
 // One wavefront per (token, kv head); lane l owns channels PER*l .. PER*l+PER-1.
+// Cache layout as documented in pa.h (bf16 K tiles store offsets in the
+// bit-2/3-exchanged slot order).
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
@@ -66,10 +68,11 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
     const uint16_t *vv = static_cast<const uint16_t *>(p.value) + src;
     uint16_t *kc = static_cast<uint16_t *>(p.k_cache);
     uint16_t *vc = static_cast<uint16_t *>(p.v_cache);
+    const int ks = bf16_k_slot(o);  // bf16 K tiles hold offset o at this slot
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int d = PER * lane + k;
-      kc[k_off<D, BS, X>(tile, o, d)] = kk[d];
+      kc[k_off<D, BS, X>(tile, ks, d)] = kk[d];
       vc[v_off<D, BS, X>(tile, o, d)] = vv[d];
     }
   } else {

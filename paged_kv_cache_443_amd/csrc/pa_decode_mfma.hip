@@ -88,6 +88,19 @@ struct Ctx {
   int32_t m, j;
 };
 
+// K/V tile loads.  bf16 tiles are read once per step and streamed past the
+// caches (non-temporal): every bf16 load covers whole 128-byte lines (K slot
+// order above), so nothing is fetched twice.  int8 K row groups cover
+// quarter lines (four tokens of each of four blocks), which non-temporal
+// loads would re-fetch: int8 tiles use ordinary loads.
+template <bool I8>
+__device__ __forceinline__ u32x4 load_kv(const u32x4 *ptr) {
+  if constexpr (I8)
+    return *ptr;
+  else
+    return __builtin_nontemporal_load(ptr);
+}
+
 // Block ids of chunk starting at position cs, read from the LDS table window.
 template <bool I8, int D, int BS>
 __device__ __forceinline__ Ids read_ids(const Ctx<I8, D, BS> &x, int cs) {
@@ -109,9 +122,10 @@ __device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x
   const u32x4 *kp = x.kpool + ktile * (D / T::X) * BS;
 #pragma unroll
   for (int q = 0; q < T::NQ; ++q) {
-    const int ok = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
+    const int off = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
+    const int ok = I8 ? off : bf16_k_slot(off);  // lanes m % 8 read one 128-byte run
 #pragma unroll
-    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = kp[(4 * s + x.j) * BS + ok];
+    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_kv<I8>(kp + (4 * s + x.j) * BS + ok);
   }
 }
 
@@ -131,7 +145,7 @@ __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x
   }
   const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) vb.v[n] = vp[16 * n];
+  for (int n = 0; n < T::ND; ++n) vb.v[n] = load_kv<I8>(vp + 16 * n);
 }
 
 template <bool I8, int D>
@@ -272,15 +286,20 @@ __device__ __forceinline__ void pv_update(State<I8, D> &st, VBuf<I8, D> &vb, con
   }
 }
 
-constexpr int kTableWindow = 1024;  // block-table entries staged in LDS at a time
+// LDS of one work-group (dynamic: sized per launch by lds_bytes()):
+//   int32 tbl[tbl_window]            block-table window
+//   float m[NW][rows], l[NW][rows]   per-wavefront softmax statistics
+//   float acc[NW][rows][D + 4]       per-wavefront output rows
+// rows = min(16, group): only the query heads the work-group owns.
+template <int D, int NW>
+__host__ __device__ constexpr size_t lds_bytes(int tbl_window, int rows) {
+  return static_cast<size_t>(tbl_window) * 4 + static_cast<size_t>(NW) * rows * (2 + D + 4) * 4;
+}
 
 template <bool I8, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   using T = Tile<I8, D>;
-  __shared__ float sm_acc[NW][16][D + 4];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ int32_t sm_tbl[kTableWindow];
+  extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -293,6 +312,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   const int kvh = hx / p.head_groups;
   const int g0 = (hx % p.head_groups) * 16;
   const int gcount = min(16, p.group - g0);
+  const int rows = min(16, p.group);
+  const int TW = p.tbl_window;
+
+  int32_t *sm_tbl = reinterpret_cast<int32_t *>(smem);
+  float *sm_m = reinterpret_cast<float *>(smem + static_cast<size_t>(TW) * 4);
+  float *sm_l = sm_m + NW * rows;
+  float *sm_acc = sm_l + NW * rows;  // [NW][rows][D + 4]
+
+  // ---- prologue: the length, the first block-table window and the queries are
+  // independent loads, issued together -----------------------------------------
+  const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const int Lraw = p.context_lens[b];
+  const bool split = p.partition_size > 0;
+  const int t0 = split ? part * p.partition_size : 0;
+  const int lb_first = t0 / BS;
+  {
+    const int n_first = min(TW, p.max_blocks_per_seq - lb_first);
+    for (int i = threadIdx.x; i < n_first; i += NW * 64) sm_tbl[i] = table[lb_first + i];
+  }
 
   Ctx<I8, D, BS> x;
   x.m = lane & 15;
@@ -305,15 +343,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm_tbl;
-  const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
-  const int L = min(max(p.context_lens[b], 0), p.max_blocks_per_seq * BS);
-  int t0 = 0;
-  x.t1 = L;
-  if (p.partition_size > 0) {
-    t0 = part * p.partition_size;
-    x.t1 = min(t0 + p.partition_size, L);
-  }
-  x.nbv = (x.t1 + BS - 1) / BS;
 
   // ---- query operand (B of the QK product): head m of the group -----------
   QOp<I8, D> qop;
@@ -330,20 +359,27 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
+  const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
+  x.t1 = split ? min(t0 + p.partition_size, L) : L;
+  x.nbv = (x.t1 + BS - 1) / BS;
+
   State<I8, D> st;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = -INFINITY;
   st.l_run = 0.f;
+  __syncthreads();  // first table window staged
 
   // ---- token range in windows of staged block-table entries (usually one) ----
-  for (int ws = t0; ws < x.t1; ws += kTableWindow * BS) {
-    const int we = min(ws + kTableWindow * BS, x.t1);
+  for (int ws = t0; ws < x.t1; ws += TW * BS) {
+    const int we = min(ws + TW * BS, x.t1);
     x.lb0 = ws / BS;
-    const int nbw = (we + BS - 1) / BS - x.lb0;
-    __syncthreads();  // readers of the previous window are done
-    for (int i = threadIdx.x; i < nbw; i += NW * 64) sm_tbl[i] = table[x.lb0 + i];
-    __syncthreads();
+    if (ws != t0) {
+      const int nbw = (we + BS - 1) / BS - x.lb0;
+      __syncthreads();  // readers of the previous window are done
+      for (int i = threadIdx.x; i < nbw; i += NW * 64) sm_tbl[i] = table[x.lb0 + i];
+      __syncthreads();
+    }
 
     // chunks ws + c*CT of this window; wave w takes c = w, w + NW, ...
     const int nch = (we - ws + T::CT - 1) / T::CT;
@@ -385,30 +421,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   // ---- merge the wavefronts' states -------------------------------------------
   float l = st.l_run + __shfl_xor(st.l_run, 16);
   l = l + __shfl_xor(l, 32);
+  if (x.m < rows) {
+    float *arow = sm_acc + (static_cast<size_t>(w) * rows + x.m) * (D + 4);
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) *reinterpret_cast<f32x4 *>(&sm_acc[w][x.m][16 * n + 4 * x.j]) = st.acc[n];
-  if (x.j == 0) {
-    sm_m[w][x.m] = st.m_run;
-    sm_l[w][x.m] = l;
+    for (int n = 0; n < T::ND; ++n) *reinterpret_cast<f32x4 *>(arow + 16 * n + 4 * x.j) = st.acc[n];
+    if (x.j == 0) {
+      sm_m[w * rows + x.m] = st.m_run;
+      sm_l[w * rows + x.m] = l;
+    }
   }
   __syncthreads();
 
-  const bool split = p.partition_size > 0;
   for (int e = threadIdx.x; e < gcount * D; e += NW * 64) {
     const int gi = e / D;
     const int d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v][gi]);
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v * rows + gi]);
     float o = 0.f;
     float lse = -INFINITY;
     if (M != -INFINITY) {
       float lsum = 0.f, osum = 0.f;
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
-        const float f = fast_exp2(sm_m[v][gi] - M);
-        lsum += f * sm_l[v][gi];
-        osum += f * sm_acc[v][gi][d];
+        const float f = fast_exp2(sm_m[v * rows + gi] - M);
+        lsum += f * sm_l[v * rows + gi];
+        osum += f * sm_acc[(static_cast<size_t>(v) * rows + gi) * (D + 4) + d];
       }
       o = osum / lsum;
       lse = (M + __log2f(lsum)) * kLn2;
@@ -432,7 +470,9 @@ hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
   constexpr int NW = 4;
   const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64), 0, s, p);
+  const size_t lds = lds_bytes<D, NW>(p.tbl_window, min(16, p.group));
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64), lds, s,
+                     p);
   return hipGetLastError();
 }
 

@@ -28,6 +28,11 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// Slot of in-block token offset t on the token axis of a bf16 K tile: bits
+// 2 and 3 exchanged, so the two 4-token runs a matrix-core row group takes
+// from every 8 tokens sit side by side (one 128-byte line per load).
+__host__ __device__ __forceinline__ int bf16_k_slot(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
 // 2^x on the transcendental unit (inputs here are <= 0 or -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -71,6 +71,27 @@ def test_layout_element_positions():
             assert vf[(((pb * H + h) * (bs // x) + t // x) * D + d) * x + t % x] == V[0, h, d]
 
 
+def test_bf16_k_slot_order():
+    """bf16 K tiles store in-block offsets in the order 0-3, 8-11, 4-7, 12-15
+    per group of 16 (the documented layout); V and other dtypes keep order."""
+    want = [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+    nb, H, bs, D = 2, 1, 32, 16
+    c = oracle.PagedCache.empty("bf16", nb, H, bs, D, poison=False)
+    for t in range(bs):
+        K = np.full((1, H, D), float(t + 1), np.float32)
+        oracle.append(c, K, K, np.array([bs + t]))
+    x = 8
+    for t in range(bs):
+        slot = 16 * (t // 16) + want[t % 16]
+        for d in range(D):
+            flat = (((1 * H + 0) * (D // x) + d // x) * bs + slot) * x + d % x
+            got = oracle.layout.bf16_bits_to_f64(c.k.reshape(-1)[flat])
+            assert got == t + 1, (t, slot, d)
+    assert list(oracle.k_slot(np.arange(16), "bf16")) == want
+    assert list(oracle.k_slot(np.arange(16), "i8")) == list(range(16))
+    assert list(oracle.k_slot(np.arange(16), "f32")) == list(range(16))
+
+
 def test_append_copies_and_skips():
     rng = np.random.default_rng(4)
     c = oracle.PagedCache.empty("bf16", 4, 2, 16, 16)
