@@ -59,6 +59,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="upper bound on the oracle's timed CPU work")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (calibrates rocprofv3 byte counters)")
     return ap.parse_args(argv)
 
 
@@ -153,15 +155,19 @@ class Case:
 
 
 class Flush:
-    """Evicts the L2s and the Infinity Cache by reading a 1 GiB buffer (a sum)."""
+    """Evicts the L2s and the Infinity Cache by reading a 1 GiB buffer.
+
+    A float32 sum into a float32 scalar: one read pass, no temporaries and no
+    dtype conversion, so the caches are left holding clean lines only.
+    """
 
     def __init__(self, torch, mib: int, device):
         self.torch = torch
-        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.int32, device=device)
-        self.sink = torch.zeros((), dtype=torch.int64, device=device)
+        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=device)
+        self.sink = torch.zeros((), dtype=torch.float32, device=device)
 
     def __call__(self):
-        self.torch.sum(self.buf, dim=0, dtype=self.torch.int64, out=self.sink)
+        self.torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
@@ -213,6 +219,45 @@ def summarise(case: Case, t: dict, peak: float) -> dict:
                   "split_scratch_overhead": case.scratch_bytes},
     }
     return d
+
+
+# --------------------------------------------------------------------------
+# HBM traffic of the dominant kernel (from rocprofv3 counter passes)
+# --------------------------------------------------------------------------
+
+KERNEL_SOURCES = ("pa_decode_mfma.hip", "pa_device.h", "pa_internal.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the decode kernel is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_443_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch recorded in profiles/ for this workload's dominant
+    kernel, or None when there is no record or the kernel sources changed since
+    the counters were taken.  Record lines: ``key: value``."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes": int(float(rec["traffic_bytes_per_launch"])), "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------------
@@ -289,6 +334,14 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     flush = Flush(torch, args.flush_mib, dev)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # plain copy: copy_probe_mib MiB read, the same written
+        torch.cuda.synchronize()
+        del src, dst
 
     others = [int(c) for c in args.others.split(",") if c.strip()] if args.others else []
     others = [c for c in others if c != args.config]
@@ -307,6 +360,7 @@ def main(argv=None) -> int:
     dec_key = "decode_split" if case.split else "decode"
     dec_bytes = case.split_kernel_bytes if case.split else case.decode_bytes
     dec_us = t[dec_key]["mean_us"]
+    traffic = measured_traffic(s.name)
     roofline = {
         "bound": "hbm",
         "kernel": head["dominant_kernel"],
@@ -314,10 +368,12 @@ def main(argv=None) -> int:
         "peak": peak,
         "unit": "GB/s",
         "frac": round(dec_bytes / dec_us / 1e3 / peak, 4),
-        "traffic": None,
+        "traffic": traffic["bytes"] if traffic else None,
         "algorithmic_bytes_per_launch": dec_bytes,
         "avg_launch_us": round(dec_us, 2),
     }
+    if traffic:
+        roofline["traffic_source"] = traffic["source"]
 
     line = {
         "metric": METRIC,

@@ -151,14 +151,15 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
  * min((p + 1) * partition_size, L)).  For each (b, h, p) it writes the
  * normalised partial output o_p = softmax restricted to that range applied
  * to V, and lse_p = natural log of sum over the range of exp(scale * q.k_t).
- * Partitions with no tokens get o_p = 0 and lse_p = -inf.
+ * Only partitions that hold tokens (p < ceil(L / partition_size)) are
+ * written; the entries of the others are left as they are (pa_reduce never
+ * reads them).  For L == 0 nothing of sequence b is written.
  *
  *   arguments up to `scale` as for pa_decode, then
  *   partition_size      tokens per partition, a positive multiple of block_size
  *   max_num_partitions  Pmax >= ceil(max_blocks_per_seq * block_size / partition_size)
  *   part_out            fp32 [num_seqs][num_heads][Pmax][head_dim], 16-byte aligned
  *   part_lse            fp32 [num_seqs][num_heads][Pmax], 4-byte aligned
- * Every (b, h, p < Pmax) entry is written.
  */
 pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
                           const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -10,10 +10,11 @@
 // scale is zero.  The divisions are IEEE fp32 (the compiler's default
 // correctly rounded division), so the result is bit-exact.
 //
-// One wavefront per (token, kv head); lane l owns channels PER*l .. PER*l+PER-1.
 // Cache layout as documented in pa.h (bf16 K tiles store offsets in the
 // bit-2/3-exchanged slot order).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -37,81 +38,101 @@ __device__ __forceinline__ size_t v_off(size_t tile, int o, int d) {
   return ((tile * (BS / X) + o / X) * D + d) * X + o % X;
 }
 
+// PER consecutive elements of type E packed in one register-sized value.
+template <typename E, int PER>
+struct Pack {
+  E e[PER];
+};
+
+template <typename E, int PER>
+__device__ __forceinline__ Pack<E, PER> load_pack(const E *ptr) {
+  return *reinterpret_cast<const Pack<E, PER> *>(ptr);
+}
+template <typename E, int PER>
+__device__ __forceinline__ void store_pack(E *ptr, const Pack<E, PER> &v) {
+  *reinterpret_cast<Pack<E, PER> *>(ptr) = v;
+}
+
+constexpr int kAppendWaves = 4;
+
+// One wavefront per (token, kv head) pair, four pairs per work-group.  Lane
+// l owns channels PER*l .. PER*l + PER - 1, which are adjacent in a K tile
+// (one store per lane) and X elements apart in a V tile.  The source rows are
+// loaded alongside the slot, so the only dependent access is the cache write.
 template <int KIND, int D, int BS>  // KIND: 0 fp32, 1 bf16, 2 int8
-__global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(AppendParams p) {
   constexpr int PER = D / 64;
   constexpr int X = KIND == 0 ? 4 : (KIND == 1 ? 8 : 16);
-  const int lane = threadIdx.x;
-  const int id = blockIdx.x;
-  const int h = id % p.num_kv_heads;
-  const int i = id / p.num_kv_heads;
+  typedef typename std::conditional<KIND == 0, float, uint16_t>::type Src;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * kAppendWaves + (threadIdx.x >> 6);
+  if (pair >= static_cast<int64_t>(p.num_tokens) * p.num_kv_heads) return;  // whole wavefront
+  const int i = static_cast<int>(pair / p.num_kv_heads);
+  const int h = static_cast<int>(pair % p.num_kv_heads);
+  const int d0 = PER * lane;
   const int32_t slot = p.slot_mapping[i];
+  const size_t src = (static_cast<size_t>(i) * p.num_kv_heads + h) * D + d0;
+  const Pack<Src, PER> kk = load_pack<Src, PER>(static_cast<const Src *>(p.key) + src);
+  const Pack<Src, PER> vv = load_pack<Src, PER>(static_cast<const Src *>(p.value) + src);
   if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(p.num_blocks) * BS) return;
   const int pb = slot / BS;
   const int o = slot % BS;
-  const size_t tile = static_cast<size_t>(pb) * p.num_kv_heads + h;
-  const size_t src = (static_cast<size_t>(i) * p.num_kv_heads + h) * D;
+  {
+    const size_t tile = static_cast<size_t>(pb) * p.num_kv_heads + h;
 
-  if constexpr (KIND == 0) {
-    const float *kk = static_cast<const float *>(p.key) + src;
-    const float *vv = static_cast<const float *>(p.value) + src;
-    float *kc = static_cast<float *>(p.k_cache);
-    float *vc = static_cast<float *>(p.v_cache);
+    if constexpr (KIND <= 1) {
+      // bf16 K tiles hold offset o at its bit-2/3-exchanged slot
+      const int ks = KIND == 1 ? bf16_k_slot(o) : o;
+      Src *kc = static_cast<Src *>(p.k_cache);
+      Src *vc = static_cast<Src *>(p.v_cache);
+      store_pack<Src, PER>(kc + k_off<D, BS, X>(tile, ks, d0), kk);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int d = PER * lane + k;
-      kc[k_off<D, BS, X>(tile, o, d)] = kk[d];
-      vc[v_off<D, BS, X>(tile, o, d)] = vv[d];
-    }
-  } else if constexpr (KIND == 1) {
-    const uint16_t *kk = static_cast<const uint16_t *>(p.key) + src;
-    const uint16_t *vv = static_cast<const uint16_t *>(p.value) + src;
-    uint16_t *kc = static_cast<uint16_t *>(p.k_cache);
-    uint16_t *vc = static_cast<uint16_t *>(p.v_cache);
-    const int ks = bf16_k_slot(o);  // bf16 K tiles hold offset o at this slot
+      for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = vv.e[k];
+    } else {
+      int8_t *kc = static_cast<int8_t *>(p.k_cache);
+      int8_t *vc = static_cast<int8_t *>(p.v_cache);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int d = PER * lane + k;
-      kc[k_off<D, BS, X>(tile, ks, d)] = kk[d];
-      vc[v_off<D, BS, X>(tile, o, d)] = vv[d];
-    }
-  } else {
-    const uint16_t *src_rows[2] = {static_cast<const uint16_t *>(p.key) + src,
-                                   static_cast<const uint16_t *>(p.value) + src};
-    int8_t *pools[2] = {static_cast<int8_t *>(p.k_cache), static_cast<int8_t *>(p.v_cache)};
-    uint16_t *scales[2] = {p.k_scale, p.v_scale};
+      for (int which = 0; which < 2; ++which) {
+        const Pack<Src, PER> &row = which == 0 ? kk : vv;
+        float xv[PER];
+        float amax = 0.f;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      float xv[PER];
-      float amax = 0.f;
+        for (int k = 0; k < PER; ++k) {
+          xv[k] = bf16_bits_to_float(row.e[k]);
+          amax = fmaxf(amax, fabsf(xv[k]));
+        }
+        amax = wave_max(amax);
+        const uint16_t s16 = float_to_half_bits(amax / 127.0f);
+        const float sf = half_bits_to_float(s16);
+        Pack<int8_t, PER> q;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        xv[k] = bf16_bits_to_float(src_rows[which][PER * lane + k]);
-        amax = fmaxf(amax, fabsf(xv[k]));
+        for (int k = 0; k < PER; ++k) {
+          float qf = 0.f;
+          if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -127.f), 127.f);
+          q.e[k] = static_cast<int8_t>(static_cast<int>(qf));
+        }
+        if (which == 0) {
+          store_pack<int8_t, PER>(kc + k_off<D, BS, X>(tile, o, d0), q);
+          if (lane == 0) p.k_scale[tile * BS + o] = s16;
+        } else {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = q.e[k];
+          if (lane == 0) p.v_scale[tile * BS + o] = s16;
+        }
       }
-      amax = wave_max(amax);
-      const uint16_t s16 = float_to_half_bits(amax / 127.0f);
-      const float sf = half_bits_to_float(s16);
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int d = PER * lane + k;
-        float qf = 0.f;
-        if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -127.f), 127.f);
-        const size_t off = which == 0 ? k_off<D, BS, X>(tile, o, d) : v_off<D, BS, X>(tile, o, d);
-        pools[which][off] = static_cast<int8_t>(static_cast<int>(qf));
-      }
-      if (lane == 0) scales[which][tile * BS + o] = s16;
     }
   }
 }
 
 template <int KIND, int D>
 hipError_t launch_bs(const AppendParams &p, hipStream_t s) {
-  const uint32_t nwg = static_cast<uint32_t>(static_cast<int64_t>(p.num_tokens) * p.num_kv_heads);
+  const int64_t pairs = static_cast<int64_t>(p.num_tokens) * p.num_kv_heads;
+  const uint32_t nwg = static_cast<uint32_t>((pairs + kAppendWaves - 1) / kAppendWaves);
+  const dim3 block(kAppendWaves * 64);
   switch (p.block_size) {
-    case 16: hipLaunchKernelGGL((append_kernel<KIND, D, 16>), dim3(nwg), dim3(64), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((append_kernel<KIND, D, 32>), dim3(nwg), dim3(64), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((append_kernel<KIND, D, 64>), dim3(nwg), dim3(64), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((append_kernel<KIND, D, 16>), dim3(nwg), block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((append_kernel<KIND, D, 32>), dim3(nwg), block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((append_kernel<KIND, D, 64>), dim3(nwg), block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeParams p) {
     t0 = part * p.partition_size;
     t1 = min(t0 + p.partition_size, L);
   }
+  if (p.partition_size > 0 && t1 <= t0) return;  // partitions past the end are left untouched
   const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float *kpool = static_cast<const float *>(p.k_cache);
   const float *vpool = static_cast<const float *>(p.v_cache);

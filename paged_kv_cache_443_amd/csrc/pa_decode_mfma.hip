@@ -34,11 +34,16 @@
 // probabilities keep ~16 significant bits; scores and accumulators are fp32.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
+
+// Sequences a persistent split launch can index from LDS (4 bytes each).
+constexpr int kMaxPersistentSeqs = 4096;
 
 template <bool I8, int D>
 struct Tile {
@@ -290,47 +295,63 @@ __device__ __forceinline__ void pv_update(State<I8, D> &st, VBuf<I8, D> &vb, con
 //   int32 tbl[tbl_window]            block-table window
 //   float m[NW][rows], l[NW][rows]   per-wavefront softmax statistics
 //   float acc[NW][rows][D + 4]       per-wavefront output rows
+//   int32 first[num_seqs + 1]        persistent split only: first piece of each sequence
 // rows = min(16, group): only the query heads the work-group owns.
 template <int D, int NW>
-__host__ __device__ constexpr size_t lds_bytes(int tbl_window, int rows) {
-  return static_cast<size_t>(tbl_window) * 4 + static_cast<size_t>(NW) * rows * (2 + D + 4) * 4;
+__host__ __device__ constexpr size_t lds_bytes(int tbl_window, int rows, int prefix_entries) {
+  return static_cast<size_t>(tbl_window) * 4 + static_cast<size_t>(NW) * rows * (2 + D + 4) * 4 +
+         static_cast<size_t>(prefix_entries) * 4;
 }
 
-template <bool I8, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
-  using T = Tile<I8, D>;
-  extern __shared__ __align__(16) unsigned char smem[];
+struct Smem {
+  int32_t *tbl;
+  float *m;
+  float *l;
+  float *acc;
+  int32_t *first;
+};
 
+template <int D, int NW>
+__device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
+  Smem sm;
+  sm.tbl = reinterpret_cast<int32_t *>(smem);
+  sm.m = reinterpret_cast<float *>(smem + static_cast<size_t>(TW) * 4);
+  sm.l = sm.m + NW * rows;
+  sm.acc = sm.l + NW * rows;  // [NW][rows][D + 4]
+  sm.first = reinterpret_cast<int32_t *>(sm.acc + static_cast<size_t>(NW) * rows * (D + 4));
+  return sm;
+}
+
+// One unit of work: (sequence b, kv head x query-head group hx[, partition]).
+// Every thread of the work-group calls it with the same arguments.  On entry
+// the LDS table window and merge buffers may be reused (the previous unit's
+// readers are past its last barrier); on exit its outputs are written.
+template <bool I8, int D, int BS, int NW>
+__device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
+  using T = Tile<I8, D>;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int HX = p.num_kv_heads * p.head_groups;
-  const int id = blockIdx.x;
-  const int hx = id % HX;
-  const int rest = id / HX;
-  const int b = rest % p.num_seqs;
-  const int part = rest / p.num_seqs;
   const int kvh = hx / p.head_groups;
   const int g0 = (hx % p.head_groups) * 16;
   const int gcount = min(16, p.group - g0);
   const int rows = min(16, p.group);
   const int TW = p.tbl_window;
-
-  int32_t *sm_tbl = reinterpret_cast<int32_t *>(smem);
-  float *sm_m = reinterpret_cast<float *>(smem + static_cast<size_t>(TW) * 4);
-  float *sm_l = sm_m + NW * rows;
-  float *sm_acc = sm_l + NW * rows;  // [NW][rows][D + 4]
+  const bool split = p.partition_size > 0;
 
   // ---- prologue: the length, the first block-table window and the queries are
   // independent loads, issued together -----------------------------------------
   const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const int Lraw = p.context_lens[b];
-  const bool split = p.partition_size > 0;
   const int t0 = split ? part * p.partition_size : 0;
   const int lb_first = t0 / BS;
   {
     const int n_first = min(TW, p.max_blocks_per_seq - lb_first);
-    for (int i = threadIdx.x; i < n_first; i += NW * 64) sm_tbl[i] = table[lb_first + i];
+    for (int i = threadIdx.x; i < n_first; i += NW * 64) sm.tbl[i] = table[lb_first + i];
   }
+  const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
+  // a partition past the end of its sequence is left untouched (uniform over
+  // the work-group, and no barrier has been reached)
+  if (split && t0 >= L) return;
 
   Ctx<I8, D, BS> x;
   x.m = lane & 15;
@@ -342,7 +363,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   x.vpool = static_cast<const u32x4 *>(p.v_cache);
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
-  x.tbl = sm_tbl;
+  x.tbl = sm.tbl;
 
   // ---- query operand (B of the QK product): head m of the group -----------
   QOp<I8, D> qop;
@@ -359,7 +380,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
-  const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
   x.t1 = split ? min(t0 + p.partition_size, L) : L;
   x.nbv = (x.t1 + BS - 1) / BS;
 
@@ -377,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     if (ws != t0) {
       const int nbw = (we + BS - 1) / BS - x.lb0;
       __syncthreads();  // readers of the previous window are done
-      for (int i = threadIdx.x; i < nbw; i += NW * 64) sm_tbl[i] = table[x.lb0 + i];
+      for (int i = threadIdx.x; i < nbw; i += NW * 64) sm.tbl[i] = table[x.lb0 + i];
       __syncthreads();
     }
 
@@ -422,12 +442,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   float l = st.l_run + __shfl_xor(st.l_run, 16);
   l = l + __shfl_xor(l, 32);
   if (x.m < rows) {
-    float *arow = sm_acc + (static_cast<size_t>(w) * rows + x.m) * (D + 4);
+    float *arow = sm.acc + (static_cast<size_t>(w) * rows + x.m) * (D + 4);
 #pragma unroll
     for (int n = 0; n < T::ND; ++n) *reinterpret_cast<f32x4 *>(arow + 16 * n + 4 * x.j) = st.acc[n];
     if (x.j == 0) {
-      sm_m[w * rows + x.m] = st.m_run;
-      sm_l[w * rows + x.m] = l;
+      sm.m[w * rows + x.m] = st.m_run;
+      sm.l[w * rows + x.m] = l;
     }
   }
   __syncthreads();
@@ -437,16 +457,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     const int d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v * rows + gi]);
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm.m[v * rows + gi]);
     float o = 0.f;
     float lse = -INFINITY;
     if (M != -INFINITY) {
       float lsum = 0.f, osum = 0.f;
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
-        const float f = fast_exp2(sm_m[v * rows + gi] - M);
-        lsum += f * sm_l[v * rows + gi];
-        osum += f * sm_acc[(static_cast<size_t>(v) * rows + gi) * (D + 4) + d];
+        const float f = fast_exp2(sm.m[v * rows + gi] - M);
+        lsum += f * sm.l[v * rows + gi];
+        osum += f * sm.acc[(static_cast<size_t>(v) * rows + gi) * (D + 4) + d];
       }
       o = osum / lsum;
       lse = (M + __log2f(lsum)) * kLn2;
@@ -465,15 +485,120 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <bool I8, int D, int BS>
-hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
-  constexpr int NW = 4;
-  const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
+// One work-group per unit: (sequence, kv head x query-head group[, partition]).
+template <bool I8, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
+  const int HX = p.num_kv_heads * p.head_groups;
+  const int nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
+  const int id = blockIdx.x;
+  const int part = id / (HX * p.num_seqs);
+  const int rest = id % (HX * p.num_seqs);
+  run_unit<I8, D, BS, NW>(p, sm, rest / HX, rest % HX, min(part, nparts - 1));
+}
+
+// KV-split pass as a persistent kernel: the grid is sized to the work-groups
+// the GPU holds at once, and work-group g takes pieces g, g + grid, ... of the
+// non-empty (sequence, kv head x query-head group, partition) pieces only, in
+// sequence order.  Each work-group first counts the pieces of every sequence
+// (ceil(L / partition_size) x head units) and prefix-sums the counts in LDS;
+// a piece index then maps to its sequence by binary search.  No work-group is
+// spent on a partition past the end of its sequence, and the pieces are of
+// near-equal size, so a static stride balances the work.
+template <bool I8, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
+  const int HX = p.num_kv_heads * p.head_groups;
+  const int B = p.num_seqs;
+  const int Lmax = p.max_blocks_per_seq * BS;
+  constexpr int NT = NW * 64;
+
+  // pieces of sequence i: first[i] .. first[i + 1] - 1 (exclusive scan of counts)
+  const int per = (B + NT - 1) / NT;  // sequences per thread, contiguous
+  const int i0 = min(static_cast<int>(threadIdx.x) * per, B);
+  const int i1 = min(i0 + per, B);
+  int run = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int L = min(max(p.context_lens[i], 0), Lmax);
+    const int c = (L + p.partition_size - 1) / p.partition_size * HX;
+    sm.first[i] = run;
+    run += c;
+  }
+  // exclusive scan of the per-thread totals across the work-group
+  __shared__ int32_t wsum[NW];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int v = 0; v < w; ++v) base += wsum[v];
+  int total = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) total += wsum[v];
+  for (int i = i0; i < i1; ++i) sm.first[i] += base;
+  if (threadIdx.x == 0) sm.first[B] = total;
+  __syncthreads();
+
+  for (int piece = blockIdx.x; piece < total; piece += gridDim.x) {
+    // sequence: the last i with first[i] <= piece (empty sequences share starts)
+    int lo = 0, hi = B;  // first[lo] <= piece < first[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.first[mid] <= piece)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int local = piece - sm.first[lo];
+    const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
+    if (n_b > 0) run_unit<I8, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
+  }
+}
+
+template <bool I8, int D, int BS, int NW>
+hipError_t launch_nw(const DecodeParams &p, hipStream_t s) {
+  const int rows = min(16, p.group);
+  const bool split = p.partition_size > 0;
+  if (split && p.num_seqs <= kMaxPersistentSeqs) {
+    const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
+    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW>;
+    int per_cu = 0, dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), NW * 64, lds);
+    if (e != hipSuccess) return e;
+    const int64_t most = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_num_partitions;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(std::max(per_cu, 1)) * cus, most));
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(NW * 64), lds, s, p);
+    return hipGetLastError();
+  }
+  const int64_t nparts = split ? p.max_num_partitions : 1;
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;
-  const size_t lds = lds_bytes<D, NW>(p.tbl_window, min(16, p.group));
+  const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, 0);
   hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64), lds, s,
                      p);
   return hipGetLastError();
+}
+
+// Wavefronts per unit.  A single-pass bf16 unit is a whole sequence: eight
+// wavefronts stream a long one twice as fast as four, which shortens the
+// tail of batches with spread-out lengths (one such work-group per CU at this
+// kernel's register use).  Split pieces are short and int8 units hold twice
+// the tokens per chunk: there four wavefronts and more work-groups per CU
+// measured faster.
+template <bool I8, int D, int BS>
+hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
+  if (!I8 && p.partition_size == 0) return launch_nw<I8, D, BS, 8>(p, s);
+  return launch_nw<I8, D, BS, 4>(p, s);
 }
 
 template <bool I8, int D>

@@ -7,11 +7,14 @@
 // (the online-softmax statistics of page "LLM推理优化", section 2.2, combined
 // across ranges).
 //
-// One work-group of 4 wavefronts per (sequence, query head).  Wavefront w
-// folds partitions w, w + 4, ... (lanes cover head_dim, 8 bytes per lane at
-// head_dim 128), loading four partitions ahead; the four wavefront sums are
-// then added in wavefront order through LDS, so the summation order is fixed
-// and the result bitwise reproducible.
+// A work-group of four wavefronts serves RPW (sequence, query head) rows;
+// each row gets W = 4 / RPW wavefronts, and wavefront w of a row folds the
+// row's partitions w, w + W, ... with kUnroll of them loaded at once (lanes
+// cover head_dim, 8 bytes per lane at head_dim 128).  Each wavefront keeps
+// its own maximum; the W partial sums are rescaled to the row maximum and
+// added in wavefront order, so the result is bitwise reproducible.  The host
+// picks RPW from max_num_partitions: many short rows pack four to a
+// work-group, a few long rows get four wavefronts each.
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
@@ -20,8 +23,8 @@
 namespace pa {
 namespace {
 
-constexpr int kRw = 4;      // wavefronts per work-group
-constexpr int kUnroll = 4;  // partitions in flight per wavefront
+constexpr int kWaves = 4;   // wavefronts per work-group
+constexpr int kUnroll = 8;  // partitions in flight per wavefront
 
 template <int VEC>
 struct Vec;
@@ -34,99 +37,139 @@ struct Vec<2> {
   typedef float2 T;
 };
 
-template <int D>
-__global__ __launch_bounds__(kRw * 64) void reduce_kernel(ReduceParams p) {
+template <int D, int RPW>
+__global__ __launch_bounds__(kWaves * 64) void reduce_kernel(ReduceParams p) {
   constexpr int VEC = D / 64;  // floats per lane
+  constexpr int W = kWaves / RPW;  // wavefronts per row
   typedef typename Vec<VEC>::T VT;
-  __shared__ float sm_max[kRw];
-  __shared__ float sm_w[kRw];
-  __shared__ float sm_acc[kRw][D];
+  __shared__ float sm_m[kWaves];
+  __shared__ float sm_l[kWaves];
+  __shared__ float sm_acc[kWaves][D];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const size_t row = blockIdx.x;  // b * num_heads + h
-  const int b = static_cast<int>(row / p.num_heads);
-  const int L = max(p.context_lens[b], 0);
-  const int n = min((L + p.partition_size - 1) / p.partition_size, p.max_num_partitions);
-  const float *lse = p.part_lse + row * p.max_num_partitions;
-  const VT *po = reinterpret_cast<const VT *>(p.part_out + row * p.max_num_partitions * D);
+  const int wave = threadIdx.x >> 6;
+  const int r = wave / W;  // row of this work-group
+  const int w = wave % W;  // wavefront within the row
+  const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_heads;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPW + r;
+  const bool live = row < rows;
 
-  // M = max over the used partitions (max is exact in any order)
-  float m = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += kRw * 64) m = fmaxf(m, lse[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) sm_max[w] = m;
-  __syncthreads();
-  float M = sm_max[0];
-#pragma unroll
-  for (int v = 1; v < kRw; ++v) M = fmaxf(M, sm_max[v]);
-
+  float m = -INFINITY, l = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
-  float wsum = 0.f;
-  if (M != -INFINITY) {
+  if (live) {
+    const int b = static_cast<int>(row / p.num_heads);
+    const int L = max(p.context_lens[b], 0);
+    const int n = min((L + p.partition_size - 1) / p.partition_size, p.max_num_partitions);
+    const float *lse = p.part_lse + row * p.max_num_partitions;
+    const VT *po = reinterpret_cast<const VT *>(p.part_out + row * p.max_num_partitions * D);
     constexpr float kLog2e = 1.4426950408889634f;
-    for (int i0 = w; i0 < n; i0 += kRw * kUnroll) {
+    for (int i0 = w; i0 < n; i0 += W * kUnroll) {
       VT v[kUnroll];
-      float l[kUnroll];
+      float ls[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int i = min(i0 + u * kRw, n - 1);
+        const int i = min(i0 + u * W, n - 1);
         v[u] = po[static_cast<size_t>(i) * 64 + lane];
-        l[u] = lse[i];
+        ls[u] = lse[i];
       }
+      float mn = m;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (i0 + u * kRw < n) {
-          const float wt = __builtin_amdgcn_exp2f((l[u] - M) * kLog2e);
-          wsum += wt;
-          if constexpr (VEC == 1) {
-            acc[0] += wt * v[u];
-          } else {
-            acc[0] += wt * v[u].x;
-            acc[1] += wt * v[u].y;
+      for (int u = 0; u < kUnroll; ++u)
+        if (i0 + u * W < n) mn = fmaxf(mn, ls[u]);
+      if (mn != -INFINITY) {
+        const float alpha = __builtin_amdgcn_exp2f((m - mn) * kLog2e);  // 0 when m is -inf
+        l *= alpha;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (i0 + u * W < n) {
+            const float wt = __builtin_amdgcn_exp2f((ls[u] - mn) * kLog2e);
+            l += wt;
+            if constexpr (VEC == 1) {
+              acc[0] += wt * v[u];
+            } else {
+              acc[0] += wt * v[u].x;
+              acc[1] += wt * v[u].y;
+            }
           }
         }
+        m = mn;
       }
     }
   }
+  if constexpr (W == 1) {
+    if (live) {
 #pragma unroll
-  for (int k = 0; k < VEC; ++k) sm_acc[w][lane * VEC + k] = acc[k];
-  if (lane == 0) sm_w[w] = wsum;
-  __syncthreads();
-  if (w == 0) {
-    float tw = 0.f;
+      for (int k = 0; k < VEC; ++k) {
+        const float o = l > 0.f ? acc[k] / l : 0.f;
+        const size_t idx = static_cast<size_t>(row) * D + lane * VEC + k;
+        if (p.out_bf16)
+          static_cast<uint16_t *>(p.out)[idx] = float_to_bf16_bits(o);
+        else
+          static_cast<float *>(p.out)[idx] = o;
+      }
+    }
+  } else {
 #pragma unroll
-    for (int v = 0; v < kRw; ++v) tw += sm_w[v];
+    for (int k = 0; k < VEC; ++k) sm_acc[wave][lane * VEC + k] = acc[k];
+    if (lane == 0) {
+      sm_m[wave] = m;
+      sm_l[wave] = l;
+    }
+    __syncthreads();
+    if (w == 0 && live) {
+      float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-      const int d = lane * VEC + k;
-      float s = 0.f;
+      for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[r * W + v]);
+      float f[W];
+      float tl = 0.f;
 #pragma unroll
-      for (int v = 0; v < kRw; ++v) s += sm_acc[v][d];
-      const float o = tw > 0.f ? s / tw : 0.f;
-      const size_t idx = row * D + d;
-      if (p.out_bf16)
-        static_cast<uint16_t *>(p.out)[idx] = float_to_bf16_bits(o);
-      else
-        static_cast<float *>(p.out)[idx] = o;
+      for (int v = 0; v < W; ++v) {
+        f[v] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((sm_m[r * W + v] - M) * 1.4426950408889634f);
+        tl += f[v] * sm_l[r * W + v];
+      }
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const int d = lane * VEC + k;
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < W; ++v) s += f[v] * sm_acc[r * W + v][d];
+        const float o = tl > 0.f ? s / tl : 0.f;
+        const size_t idx = static_cast<size_t>(row) * D + d;
+        if (p.out_bf16)
+          static_cast<uint16_t *>(p.out)[idx] = float_to_bf16_bits(o);
+        else
+          static_cast<float *>(p.out)[idx] = o;
+      }
     }
   }
+}
+
+template <int D, int RPW>
+hipError_t launch_r(const ReduceParams &p, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_heads;
+  const uint32_t nwg = static_cast<uint32_t>((rows + RPW - 1) / RPW);
+  hipLaunchKernelGGL((reduce_kernel<D, RPW>), dim3(nwg), dim3(kWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const ReduceParams &p, hipStream_t s) {
+  // one wavefront per row while it can hold every partition in flight at once
+  if (p.max_num_partitions <= kUnroll) return launch_r<D, 4>(p, s);
+  if (p.max_num_partitions <= 2 * kUnroll) return launch_r<D, 2>(p, s);
+  return launch_r<D, 1>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s) {
-  const uint32_t nwg = static_cast<uint32_t>(static_cast<int64_t>(p.num_seqs) * p.num_heads);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(reduce_kernel<128>, dim3(nwg), dim3(kRw * 64), 0, s, p);
-  else if (p.head_dim == 64)
-    hipLaunchKernelGGL(reduce_kernel<64>, dim3(nwg), dim3(kRw * 64), 0, s, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.head_dim == 128) return launch_d<128>(p, s);
+  if (p.head_dim == 64) return launch_d<64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa
