@@ -44,6 +44,9 @@ namespace {
 
 // Sequences a persistent split launch can index from LDS (4 bytes each).
 constexpr int kMaxPersistentSeqs = 4096;
+// Sequences a single-pass launch ranks by length in every work-group (the
+// ranking costs num_seqs^2 / threads LDS reads per work-group).
+constexpr int kMaxLptSeqs = 512;
 
 template <bool I8, int D>
 struct Tile {
@@ -322,11 +325,96 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
   return sm;
 }
 
+// Consume one chunk held in (kb, vb): QK, online softmax, PV.  With REFILL,
+// the next loads into the same buffers are issued as soon as each buffer is
+// read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
+// (sched_barrier pins the load issue points: left alone, the scheduler sinks
+// them next to their first use and nothing stays in flight.)
+template <bool I8, int D, int BS, bool TAIL, bool REFILL>
+__device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<I8, D> &vb,
+                                        const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop, int cs, int cn, Ids idn,
+                                        float scale_log2) {
+  using T = Tile<I8, D>;
+  Scores<I8, D> S;
+  Probs<I8, D> P;
+  qk<I8, D>(S, kb, qop);
+  if constexpr (REFILL) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k(kb, x, cn, idn);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  softmax<I8, D, TAIL>(st, S, vb, P, cs + T::TPL * x.j, x.t1, scale_log2);
+  pv_update<I8, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  if constexpr (REFILL) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_v(vb, x, cn, idn);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
+// while the previous one is computed.
+template <bool I8, int D, int BS, int NW>
+__device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
+                                                int c0, int n, float scale_log2) {
+  constexpr int STEP = NW * Tile<I8, D>::CT;
+  KBuf<I8, D> kb;
+  VBuf<I8, D> vb;
+  int cs = c0;
+  const Ids ids = read_ids(x, cs);
+  issue_k(kb, x, cs, ids);
+  issue_v(vb, x, cs, ids);
+  for (int k = 0; k + 1 < n; ++k) {
+    const int cn = cs + STEP;
+    consume<I8, D, BS, false, true>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+    cs = cn;
+  }
+  consume<I8, D, BS, true, false>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
+}
+
+// The same with two chunks in flight: buffers A and B alternate; chunk i is in
+// A for even i and in B for odd i.
+template <bool I8, int D, int BS, int NW>
+__device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
+                                                int c0, int n, float scale_log2) {
+  constexpr int STEP = NW * Tile<I8, D>::CT;
+  KBuf<I8, D> ka, kb;
+  VBuf<I8, D> va, vb;
+  {
+    const Ids i0 = read_ids(x, c0);
+    issue_k(ka, x, c0, i0);
+    issue_v(va, x, c0, i0);
+    if (n > 1) {
+      const Ids i1 = read_ids(x, c0 + STEP);
+      issue_k(kb, x, c0 + STEP, i1);
+      issue_v(vb, x, c0 + STEP, i1);
+    }
+  }
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    const int ci = c0 + i * STEP;
+    consume<I8, D, BS, false, true>(st, ka, va, x, qop, ci, ci + 2 * STEP, read_ids(x, ci + 2 * STEP), scale_log2);
+    if (i + 3 < n)
+      consume<I8, D, BS, false, true>(st, kb, vb, x, qop, ci + STEP, ci + 3 * STEP, read_ids(x, ci + 3 * STEP),
+                                      scale_log2);
+    else
+      consume<I8, D, BS, false, false>(st, kb, vb, x, qop, ci + STEP, 0, Ids{0, 0}, scale_log2);
+  }
+  // chunk i is in A; chunk i + 1, if any, is in B and is the last one
+  const int ci = c0 + i * STEP;
+  if (i + 1 < n) {
+    consume<I8, D, BS, false, false>(st, ka, va, x, qop, ci, 0, Ids{0, 0}, scale_log2);
+    consume<I8, D, BS, true, false>(st, kb, vb, x, qop, ci + STEP, 0, Ids{0, 0}, scale_log2);
+  } else {
+    consume<I8, D, BS, true, false>(st, ka, va, x, qop, ci, 0, Ids{0, 0}, scale_log2);
+  }
+}
+
 // One unit of work: (sequence b, kv head x query-head group hx[, partition]).
 // Every thread of the work-group calls it with the same arguments.  On entry
 // the LDS table window and merge buffers may be reused (the previous unit's
 // readers are past its last barrier); on exit its outputs are written.
-template <bool I8, int D, int BS, int NW>
+template <bool I8, int D, int BS, int NW, int DEPTH>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<I8, D>;
   const int lane = threadIdx.x & 63;
@@ -405,36 +493,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int nch = (we - ws + T::CT - 1) / T::CT;
     const int n = w < nch ? (nch - w + NW - 1) / NW : 0;
     if (n > 0) {
-      KBuf<I8, D> kb;
-      VBuf<I8, D> vb;
-      Scores<I8, D> S;
-      Probs<I8, D> P;
-      int cs = ws + w * T::CT;
-      Ids ids = read_ids(x, cs);
-      issue_k(kb, x, cs, ids);
-      issue_v(vb, x, cs, ids);
-      // steady state: K of the next chunk loads during this chunk's softmax and
-      // PV, V of the next chunk during the next chunk's QK
-      // (sched_barrier pins the load issue points: left alone, the scheduler
-      // sinks them next to their first use and nothing stays in flight)
-      for (int k = 0; k + 1 < n; ++k) {
-        const int cn = cs + NW * T::CT;
-        const Ids idn = read_ids(x, cn);
-        qk<I8, D>(S, kb, qop);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_k(kb, x, cn, idn);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax<I8, D, false>(st, S, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
-        pv_update<I8, D, false>(st, vb, P, cs + T::TPL * x.j, x.t1);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_v(vb, x, cn, idn);
-        __builtin_amdgcn_sched_barrier(0);
-        cs = cn;
-      }
-      // last chunk of this wave (the only one that can reach past t1)
-      qk<I8, D>(S, kb, qop);
-      softmax<I8, D, true>(st, S, vb, P, cs + T::TPL * x.j, x.t1, p.scale_log2);
-      pv_update<I8, D, true>(st, vb, P, cs + T::TPL * x.j, x.t1);
+      if constexpr (DEPTH == 1)
+        stream_chunks_1<I8, D, BS, NW>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
+      else
+        stream_chunks_2<I8, D, BS, NW>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
     }
   }
 
@@ -486,7 +548,13 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 }
 
 // One work-group per unit: (sequence, kv head x query-head group[, partition]).
-template <bool I8, int D, int BS, int NW>
+// LPT: a single pass over at most kMaxLptSeqs sequences takes the sequences
+// longest first.  The hardware hands out work-groups in index order, so the
+// last ones dispatched set the tail of the launch; with the longest units
+// first the tail is made of the shortest ones.  Every work-group ranks the
+// lengths in LDS (ties by index) and serves the sequence whose rank is its
+// index / (head units); the output is the same for any order.
+template <bool I8, int D, int BS, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
@@ -495,7 +563,41 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   const int id = blockIdx.x;
   const int part = id / (HX * p.num_seqs);
   const int rest = id % (HX * p.num_seqs);
-  run_unit<I8, D, BS, NW>(p, sm, rest / HX, rest % HX, min(part, nparts - 1));
+  int b = rest / HX;
+  if (p.lpt) {
+    constexpr int NT = NW * 64;
+    const int B = p.num_seqs;
+    const int Lmax = p.max_blocks_per_seq * BS;
+    int32_t *len = sm.first;  // len[0..B) lengths, len[B] the chosen sequence
+    for (int i = threadIdx.x; i < B; i += NT) len[i] = min(max(p.context_lens[i], 0), Lmax);
+    __syncthreads();
+    // rank of sequence i = number of sequences ahead of it; `parts` adjacent
+    // lanes share one i, each counting a slice of the others, and every
+    // thread runs the same number of passes (the shuffles need whole groups)
+    int parts = 1;
+    while (parts < 16 && parts * 2 * B <= NT) parts *= 2;
+    const int slice = threadIdx.x % parts;
+    const int per = (B + parts - 1) / parts;
+    const int groups = NT / parts;
+    const int passes = (B + groups - 1) / groups;
+    for (int k = 0; k < passes; ++k) {
+      const int i0 = k * groups + static_cast<int>(threadIdx.x) / parts;
+      const int i = min(i0, B - 1);
+      const int li = len[i];
+      const int j1 = min((slice + 1) * per, B);
+      int r = 0;
+#pragma unroll 8
+      for (int j = slice * per; j < j1; ++j) {
+        const int lj = len[j];
+        r += (lj > li) | ((lj == li) & (j < i));
+      }
+      for (int off = 1; off < parts; off <<= 1) r += __shfl_xor(r, off);
+      if (i0 < B && slice == 0 && r == b) len[B] = i;  // exactly one sequence has rank b
+    }
+    __syncthreads();
+    b = len[B];
+  }
+  run_unit<I8, D, BS, NW, DEPTH>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -506,7 +608,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // a piece index then maps to its sequence by binary search.  No work-group is
 // spent on a partition past the end of its sequence, and the pieces are of
 // near-equal size, so a static stride balances the work.
-template <bool I8, int D, int BS, int NW>
+template <bool I8, int D, int BS, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
@@ -559,17 +661,18 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
     }
     const int local = piece - sm.first[lo];
     const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
-    if (n_b > 0) run_unit<I8, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
+    if (n_b > 0) run_unit<I8, D, BS, NW, DEPTH>(p, sm, lo, local / n_b, local % n_b);
   }
 }
 
-template <bool I8, int D, int BS, int NW>
-hipError_t launch_nw(const DecodeParams &p, hipStream_t s) {
+// Split pass: persistent when the sequences' piece offsets fit in LDS,
+// else one work-group per (unit, partition).
+template <bool I8, int D, int BS, int NW, int DEPTH>
+hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   const int rows = min(16, p.group);
-  const bool split = p.partition_size > 0;
-  if (split && p.num_seqs <= kMaxPersistentSeqs) {
+  if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
-    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW>;
+    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW, DEPTH>;
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -581,11 +684,26 @@ hipError_t launch_nw(const DecodeParams &p, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(NW * 64), lds, s, p);
     return hipGetLastError();
   }
-  const int64_t nparts = split ? p.max_num_partitions : 1;
-  const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * nparts;
+  const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_num_partitions;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64), lds, s,
-                     p);
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
+                     lds, s, p);
+  return hipGetLastError();
+}
+
+// Single pass: one work-group per unit.  Longest sequences first when the
+// batch is small enough to rank in every work-group and the CU holds more
+// than one work-group, so that another one streams while a work-group ranks
+// (measured: +3 points for four-wave int8 units; with one eight-wave
+// work-group per CU the ranking is dead time and cost 2 points).
+template <bool I8, int D, int BS, int NW, int DEPTH>
+hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
+  DecodeParams p = p_in;
+  p.lpt = (NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
+  const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
+  const size_t lds = lds_bytes<D, NW>(p.tbl_window, min(16, p.group), p.lpt ? p.num_seqs + 1 : 0);
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
+                     lds, s, p);
   return hipGetLastError();
 }
 
@@ -597,8 +715,13 @@ hipError_t launch_nw(const DecodeParams &p, hipStream_t s) {
 // measured faster.
 template <bool I8, int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
-  if (!I8 && p.partition_size == 0) return launch_nw<I8, D, BS, 8>(p, s);
-  return launch_nw<I8, D, BS, 4>(p, s);
+  if constexpr (I8) {
+    if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
+    return launch_single<I8, D, BS, 4, 1>(p, s);
+  } else {
+    if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
+    return launch_single<I8, D, BS, 8, 1>(p, s);
+  }
 }
 
 template <bool I8, int D>

@@ -32,6 +32,7 @@ struct DecodeParams {
   int32_t partition_size;     // 0: whole sequence (pa_decode)
   int32_t max_num_partitions;
   int32_t tbl_window;         // block-table entries staged in LDS at a time (multiple of 4)
+  int32_t lpt;                // single pass: take sequences longest first (ranked in LDS)
   float scale;                // softmax scale as given
   float scale_log2;           // scale * log2(e)
   int32_t out_bf16;           // 1: bf16 output, 0: fp32 output
