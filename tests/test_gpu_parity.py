@@ -233,3 +233,126 @@ def test_full_size_sampled(cfg):
     err = max_err(out[picks], want)
     say(f"  sampled seqs {picks}: max abs err {err:.3e}")
     assert err <= TOL[s.kv_dtype]
+
+
+def test_int8_full_cache_fill_bit_exact():
+    """The whole int8 workload (about 1.1 M tokens x 8 kv heads) written by
+    pa_reshape_and_cache equals the oracle's quantised cache bit for bit."""
+    w = make_workload(5)
+    say(f"[fill] cfg5 full B={w.B} tokens={w.total_tokens()} pool={w.num_blocks}")
+    cache = poisoned_cache(w)
+    gpu_append_tokens(w, cache)
+    torch.cuda.synchronize()
+    k, v, ks, vs = download_cache(cache)
+    del cache
+    torch.cuda.empty_cache()
+    oc = oracle.build_cache(w, poison=True)
+    used = w.used_blocks()
+    say(f"  comparing {len(used)} used blocks")
+    assert np.array_equal(k[used], oc.k[used])
+    assert np.array_equal(v[used], oc.v[used])
+    assert np.array_equal(ks[used].view(np.uint16), oc.k_scale[used].view(np.uint16))
+    assert np.array_equal(vs[used].view(np.uint16), oc.v_scale[used].view(np.uint16))
+
+
+def test_invalid_calls_touch_nothing():
+    """A call the host validation rejects returns its status and launches
+    nothing: sentinel outputs and caches stay as they were."""
+    from paged_kv_cache_443_amd import _lib
+    import ctypes
+    say("[abi] invalid calls on device buffers")
+    w = make_workload(3, small=True)
+    cache = upload_oracle_cache(oracle.build_cache(w))
+    q, tables, lens = meta(w)
+    out = torch.full(q.shape, SENTINEL, dtype=torch.float32, device=DEV)
+    L = _lib.lib()
+    desc = cache.descriptor()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    B, Hq, D = q.shape
+    # num_heads not a multiple of num_kv_heads
+    st = L.pa_decode(q.data_ptr(), _lib.PA_BF16, B, Hq - 1, ctypes.byref(desc), tables.data_ptr(), tables.shape[1],
+                     lens.data_ptr(), 0.1, out.data_ptr(), _lib.PA_F32, stream)
+    assert st == _lib.PA_ERR_BAD_SHAPE
+    # out misaligned by 4 bytes
+    st = L.pa_decode(q.data_ptr(), _lib.PA_BF16, B, Hq, ctypes.byref(desc), tables.data_ptr(), tables.shape[1],
+                     lens.data_ptr(), 0.1, out.data_ptr() + 4, _lib.PA_F32, stream)
+    assert st == _lib.PA_ERR_MISALIGNED
+    # fp32 queries against a bf16 cache
+    st = L.pa_decode(q.data_ptr(), _lib.PA_F32, B, Hq, ctypes.byref(desc), tables.data_ptr(), tables.shape[1],
+                     lens.data_ptr(), 0.1, out.data_ptr(), _lib.PA_F32, stream)
+    assert st == _lib.PA_ERR_UNSUPPORTED
+    # append with the wrong source dtype must not write the cache
+    before = cache.k_cache.clone()
+    kn = torch.zeros((2, w.spec.Hkv, w.spec.D), dtype=torch.float32, device=DEV)
+    sl = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    st = L.pa_reshape_and_cache(kn.data_ptr(), kn.data_ptr(), _lib.PA_F32, sl.data_ptr(), 2, ctypes.byref(desc),
+                                stream)
+    assert st == _lib.PA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out == SENTINEL)
+    assert torch.equal(before.view(torch.int16), cache.k_cache.view(torch.int16))  # bitwise: the pool holds NaN poison
+
+
+def test_side_stream_matches_default_stream():
+    """The binding launches on torch's current stream: a decode issued on a
+    side stream gives the same bits as on the default stream."""
+    w = make_workload(2, small=True)
+    say("[stream] cfg2 small on a side stream")
+    cache = upload_oracle_cache(oracle.build_cache(w))
+    ref = _decode_gpu(w, cache)
+    q, tables, lens = meta(w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+        pa.decode(q, cache, tables, lens, w.spec.scale, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_graph_replays_match_eager(cfg):
+    """A decode step (append + decode, or append + split + merge) captured in a
+    HIP graph replays to the eager result every time, with eager work between
+    the replays."""
+    w = make_workload(cfg, small=True)
+    s = w.spec
+    say(f"[graph] cfg{cfg} small")
+    cache = poisoned_cache(w)
+    gpu_append_tokens(w, cache, include_last=False)
+    from workloads.device import new_token_batch
+    kn, vn, sl = new_token_batch(w)
+    q, tables, lens = meta(w)
+    P = s.partition_size or 256
+    pmax = pa.max_partitions(tables.shape[1], s.bs, P)
+    B, Hq, D = q.shape
+    po = torch.zeros((B, Hq, pmax, D), dtype=torch.float32, device=DEV)
+    pl = torch.zeros((B, Hq, pmax), dtype=torch.float32, device=DEV)
+    out = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+
+    def step():
+        pa.reshape_and_cache(kn, vn, sl, cache)
+        if s.partition_size:
+            pa.decode_split(q, cache, tables, lens, s.scale, P, po, pl)
+            pa.reduce(po, pl, lens, P, out)
+        else:
+            pa.decode(q, cache, tables, lens, s.scale, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.fill_(float("nan"))
+        _decode_gpu(w, cache)  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
