@@ -96,17 +96,18 @@ struct Ctx {
   int32_t m, j;
 };
 
-// K/V tile loads.  bf16 tiles are read once per step and streamed past the
-// caches (non-temporal): every bf16 load covers whole 128-byte lines (K slot
-// order above), so nothing is fetched twice.  int8 K row groups cover
-// quarter lines (four tokens of each of four blocks), which non-temporal
-// loads would re-fetch: int8 tiles use ordinary loads.
-template <bool I8>
-__device__ __forceinline__ u32x4 load_kv(const u32x4 *ptr) {
-  if constexpr (I8)
-    return *ptr;
-  else
+// K/V tile loads.  Tiles are read once per step and streamed past the caches
+// (non-temporal) wherever a load instruction covers whole 128-byte lines, so
+// that nothing is fetched twice: every bf16 load (K slot order above) and
+// every V load.  int8 K row groups cover quarter lines (four tokens of each
+// of four blocks); the four row-group loads of a chunk share those lines,
+// so int8 K uses ordinary loads and the lines stay in L2 between them.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load_tile(const u32x4 *ptr) {
+  if constexpr (STREAM)
     return __builtin_nontemporal_load(ptr);
+  else
+    return *ptr;
 }
 
 // Block ids of chunk starting at position cs, read from the LDS table window.
@@ -133,7 +134,7 @@ __device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x
     const int off = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
     const int ok = I8 ? off : bf16_k_slot(off);  // lanes m % 8 read one 128-byte run
 #pragma unroll
-    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_kv<I8>(kp + (4 * s + x.j) * BS + ok);
+    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_tile<!I8>(kp + (4 * s + x.j) * BS + ok);
   }
 }
 
@@ -153,7 +154,7 @@ __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x
   }
   const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) vb.v[n] = load_kv<I8>(vp + 16 * n);
+  for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<true>(vp + 16 * n);
 }
 
 template <bool I8, int D>
