@@ -26,6 +26,11 @@ another precision):
   (token, kv head) (INT8 KV cache: page "字节跳动 AI Infra (2)", optimisation
   table; page "LLM推理优化", section 1.3).
 
+* ``copy_blocks`` / ``BlockManager``: copying physical blocks, and the
+  reference counts, on-demand allocation, fork and copy-on-write of a block
+  pool (page "字节跳动 AI Infra (2)", PagedAttention question, block-pool
+  figure; page "LLM推理优化", section 3.2).
+
 Parity status: every function here is pinned by tests that do not re-use
 its own code path (closed forms, invariants, pure-Python brute force, the
 pages' worked block counts); see ``tests/test_oracle_pins.py``.
@@ -43,3 +48,4 @@ from .paged import (  # noqa: F401
     build_cache,
 )
 from .brute import decode_bruteforce  # noqa: F401
+from .blocks import BlockManager, OutOfBlocks, copy_blocks  # noqa: F401
