@@ -199,6 +199,39 @@ def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
     return r
 
 
+def time_copy_blocks(case: Case, steps: int, warmup: int, flush, max_pairs: int = 1024) -> dict:
+    """pa_copy_blocks on the workload's pool: used blocks copied into unused ones
+    (the copy of copy-on-write, at a batch size that fills the GPU)."""
+    torch, pa = case.torch, case.pa
+    import numpy as np
+
+    used = case.w.used_blocks()
+    free = np.setdiff1d(np.arange(case.w.num_blocks), used)
+    n = int(min(max_pairs, len(used), len(free)))
+    if n == 0:
+        return {}
+    rng = np.random.default_rng(5)
+    pairs = np.stack([rng.choice(used, n, replace=False), rng.choice(free, n, replace=False)], axis=1)
+    dev_pairs = torch.from_numpy(pairs.astype(np.int32)).to(case.q.device)
+    for _ in range(warmup):
+        flush()
+        pa.copy_blocks(case.cache, dev_pairs)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        pa.copy_blocks(case.cache, dev_pairs)
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    s = case.s
+    elem = {"f32": 4, "bf16": 2, "i8": 1}[s.kv_dtype]
+    per_block = s.Hkv * s.bs * s.D * elem * 2 + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype == "i8" else 0)
+    moved = n * per_block * 2 + n * 8  # read and written, plus the pairs
+    return {"pairs": n, "bytes": moved, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}
+
+
 def summarise(case: Case, t: dict, peak: float) -> dict:
     s = case.s
     step_us = t["step"]["mean_us"]
@@ -225,17 +258,23 @@ def summarise(case: Case, t: dict, peak: float) -> dict:
 # HBM traffic of the dominant kernel (from rocprofv3 counter passes)
 # --------------------------------------------------------------------------
 
-KERNEL_SOURCES = ("pa_decode_mfma.hip", "pa_device.h", "pa_internal.h")
+KERNEL_SOURCES = ("pa_decode_mfma.hip", "pa_device.h")
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the sources the decode kernel is built from."""
+    """sha256 over what the decode kernels are built from: their source file,
+    the device helpers and the parameter struct they take."""
     import hashlib
+    import re
 
+    csrc = os.path.join(ROOT, "paged_kv_cache_443_amd", "csrc")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_443_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "pa_internal.h"), encoding="utf-8") as f:
+        m = re.search(r"struct DecodeParams \{.*?\};", f.read(), re.S)
+    h.update(m.group(0).encode() if m else b"")
     return h.hexdigest()
 
 
@@ -355,6 +394,8 @@ def main(argv=None) -> int:
         f"({100 * head['step_frac_of_peak']:.1f}% of {peak:.0f}); dominant kernel "
         f"{head['dominant_GBps']} GB/s")
     out32 = case.decode_f32().cpu().numpy()
+    copy_stats = time_copy_blocks(case, args.steps, args.warmup, flush)
+    log(f"copy_blocks: {copy_stats}")
 
     s = case.s
     dec_key = "decode_split" if case.split else "decode"
@@ -399,6 +440,7 @@ def main(argv=None) -> int:
         "kernel_us": head["kernel_us"],
         "bytes_per_step": head["bytes"],
         "roofline": roofline,
+        "copy_blocks": copy_stats,
     }
 
     if not args.no_cpu_baseline:

@@ -17,9 +17,11 @@
  * - Every pointer argument except `cache` and `stream` is a DEVICE pointer
  *   (HBM of the GPU that is current when the call is made).  `cache` is a
  *   host pointer to a descriptor holding device pointers.
- * - The caller owns all memory.  The library allocates nothing, frees
- *   nothing, copies nothing to the host and never synchronises; it keeps no
- *   state except a thread-local copy of the last HIP error.
+ * - The caller owns all memory.  The library allocates no device memory,
+ *   frees nothing of the caller's, copies nothing to the host and never
+ *   synchronises; it keeps no state except a thread-local copy of the last
+ *   HIP error.  (The host block manager's bookkeeping lives in host memory
+ *   that pa_bm_create allocates and pa_bm_destroy frees.)
  * - Every call validates its host-visible arguments, then enqueues its
  *   kernels on `stream` and returns.  PA_OK means "valid and launched", not
  *   "finished".  On an error status nothing is launched and no output is
@@ -70,7 +72,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3,   /* a valid but unimplemented combination (dtype, head_dim, block_size) */
   PA_ERR_MISALIGNED = 4,    /* a pointer breaks the stated alignment */
   PA_ERR_BAD_WORKSPACE = 5, /* split scratch too small for the call */
-  PA_ERR_HIP = 6            /* the HIP launch failed; see pa_last_hip_error() */
+  PA_ERR_HIP = 6,           /* the HIP launch failed; see pa_last_hip_error() */
+  PA_ERR_OUT_OF_BLOCKS = 7, /* block manager: not enough free blocks (nothing changed) */
+  PA_ERR_INVALID_BLOCK = 8  /* block manager: a block id out of range or not in use (nothing changed) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
@@ -178,6 +182,64 @@ pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int
 pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
                     int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
                     int32_t partition_size, void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks (the copy of copy-on-write).
+ *
+ * Sequences may share physical blocks (a forked beam shares its parent's
+ * blocks); before one of them writes into a shared block, the block is
+ * copied into a private one (page "字节跳动 AI Infra (2)", PagedAttention
+ * question, block-pool figure: two beams share B1 and B3, the second writes
+ * into B6', a copy of B6; page "LLM推理优化", section 3.2).  For each
+ * i < num_pairs, block block_pairs[2i] (source) is copied to block
+ * block_pairs[2i + 1] (destination): every K and V element of every kv head
+ * and, for int8 caches, every scale.
+ *
+ *   cache        the pool (any dtype)
+ *   block_pairs  int32 [num_pairs][2] (source, destination), device, 4-byte aligned
+ * Preconditions (device data): destinations distinct, no destination also a
+ * source in the same call (then every copy reads the pool as it was before
+ * the call); pairs with an id outside [0, num_blocks) are skipped.
+ * num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs, hipStream_t stream);
+
+/*
+ * Block manager -- host bookkeeping of a block pool (no GPU work).
+ *
+ * Reference counts of num_blocks physical blocks of block_size tokens.  Blocks
+ * are handed out on demand as sequences grow (page "LLM推理优化", section 3.2:
+ * 100, 50 and 200 tokens take 7, 4 and 13 blocks of 16); a fork shares every
+ * block of a table; a write into a block that another table still references
+ * first moves the writer to a private copy (copy-on-write; the copy itself is
+ * pa_copy_blocks).  Free blocks are handed out lowest id first.  All pointers
+ * are HOST pointers.  A manager is not thread-safe; every call either
+ * succeeds or leaves the manager unchanged.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Create a manager (host memory, owned by the caller until pa_bm_destroy). */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+/* Free blocks; references held on block b (-1 if b is out of range). */
+int32_t pa_bm_num_free(const pa_block_manager *bm);
+int32_t pa_bm_refcount(const pa_block_manager *bm, int32_t block);
+/* n free blocks, lowest ids first, one reference each, into ids_out[n]. */
+pa_status pa_bm_allocate(pa_block_manager *bm, int32_t n, int32_t *ids_out);
+/* Drop one reference to each of ids[n] (all must be in use). */
+pa_status pa_bm_free(pa_block_manager *bm, const int32_t *ids, int32_t n);
+/* One more reference to each of table[n] (all must be in use): a fork. */
+pa_status pa_bm_fork(pa_block_manager *bm, const int32_t *table, int32_t n);
+/*
+ * Make room for the token at position `length` of a sequence whose block
+ * table is table[*table_len] (capacity entries available).  A position that
+ * starts a block takes a new block (appended, *table_len + 1); a position in
+ * a block that another table also references moves this table to a fresh
+ * block and reports the copy in copy_pair[0] (source), copy_pair[1]
+ * (destination), else both are -1.  *slot_out = block * block_size + offset.
+ */
+pa_status pa_bm_append_slot(pa_block_manager *bm, int32_t *table, int32_t *table_len, int32_t capacity,
+                            int32_t length, int32_t *slot_out, int32_t *copy_pair);
 
 /* Bytes of part_out plus part_lse for pa_decode_split (lse placed at a
  * 256-byte aligned offset after part_out).  0 on invalid sizes. */

@@ -27,6 +27,9 @@ __all__ = [
     "reduce",
     "split_workspace_bytes",
     "max_partitions",
+    "copy_blocks",
+    "BlockManager",
+    "OutOfBlocks",
 ]
 
 _DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
@@ -202,3 +205,86 @@ def reduce(part_out: torch.Tensor, part_lse: torch.Tensor, context_lens: torch.T
 
 def split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_num_partitions: int) -> int:
     return int(_lib.lib().pa_split_workspace_bytes(num_seqs, num_heads, head_dim, max_num_partitions))
+
+
+def copy_blocks(cache: KVCache, block_pairs: torch.Tensor) -> None:
+    """Copy whole physical blocks: ``block_pairs`` int32 ``[n, 2]`` (source, destination) on the device."""
+    _need(block_pairs, "block_pairs", torch.int32)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    desc = cache.descriptor()
+    st = _lib.lib().pa_copy_blocks(ctypes.byref(desc), _ptr(block_pairs), block_pairs.shape[0],
+                                   _stream(block_pairs.device))
+    _check("pa_copy_blocks", st)
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def _i32_array(values):
+    n = len(values)
+    arr = (ctypes.c_int32 * max(n, 1))(*values)
+    return arr, n
+
+
+class BlockManager:
+    """Host bookkeeping of a block pool through the library's C++ block manager.
+
+    Reference counts, on-demand allocation (lowest free id first), fork and
+    copy-on-write; ``append_slot`` returns the slot for a sequence's next
+    token and the (source, destination) block copies to run first
+    (``copy_blocks``).  Tables are Python lists of block ids.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = ctypes.c_void_p()
+        self.block_size = int(block_size)
+        st = _lib.lib().pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(self._h))
+        _check("pa_bm_create", st)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.lib().pa_bm_destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _raise(fn: str, st: int) -> None:
+        if st == _lib.PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(fn, st)
+        _check(fn, st)
+
+    def num_free(self) -> int:
+        return int(_lib.lib().pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.lib().pa_bm_refcount(self._h, int(block)))
+
+    def allocate(self, n: int):
+        arr, _ = _i32_array([0] * n)
+        self._raise("pa_bm_allocate", _lib.lib().pa_bm_allocate(self._h, int(n), arr))
+        return [int(arr[i]) for i in range(n)]
+
+    def free(self, ids) -> None:
+        arr, n = _i32_array(list(ids))
+        self._raise("pa_bm_free", _lib.lib().pa_bm_free(self._h, arr, n))
+
+    def fork(self, table):
+        arr, n = _i32_array(list(table))
+        self._raise("pa_bm_fork", _lib.lib().pa_bm_fork(self._h, arr, n))
+        return list(table)
+
+    def append_slot(self, table: list, length: int):
+        """Room for the token at position ``length``; ``table`` is updated in place.
+        Returns (slot, copies) with copies a list of (source, destination)."""
+        cap = len(table) + 1
+        arr, _ = _i32_array(list(table) + [0])
+        tlen = ctypes.c_int32(len(table))
+        slot = ctypes.c_int32(0)
+        pair = (ctypes.c_int32 * 2)()
+        self._raise("pa_bm_append_slot", _lib.lib().pa_bm_append_slot(
+            self._h, arr, ctypes.byref(tlen), cap, int(length), ctypes.byref(slot), pair))
+        table[:] = [int(arr[i]) for i in range(tlen.value)]
+        copies = [(int(pair[0]), int(pair[1]))] if pair[0] >= 0 else []
+        return int(slot.value), copies

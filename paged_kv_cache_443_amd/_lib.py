@@ -16,6 +16,8 @@ PA_ERR_UNSUPPORTED = 3
 PA_ERR_MISALIGNED = 4
 PA_ERR_BAD_WORKSPACE = 5
 PA_ERR_HIP = 6
+PA_ERR_OUT_OF_BLOCKS = 7
+PA_ERR_INVALID_BLOCK = 8
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -26,6 +28,15 @@ EXPORTED = (
     "pa_decode",
     "pa_decode_split",
     "pa_reduce",
+    "pa_copy_blocks",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_num_free",
+    "pa_bm_refcount",
+    "pa_bm_allocate",
+    "pa_bm_free",
+    "pa_bm_fork",
+    "pa_bm_append_slot",
     "pa_split_workspace_bytes",
     "pa_status_string",
     "pa_last_hip_error",
@@ -72,6 +83,25 @@ def lib() -> ctypes.CDLL:
     L.pa_reduce.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                             c_int, c_void_p]
     L.pa_reduce.restype = c_int
+    L.pa_copy_blocks.argtypes = [P, c_void_p, c_int32, c_void_p]
+    L.pa_copy_blocks.restype = c_int
+    I32P = ctypes.POINTER(c_int32)
+    L.pa_bm_create.argtypes = [c_int32, c_int32, ctypes.POINTER(c_void_p)]
+    L.pa_bm_create.restype = c_int
+    L.pa_bm_destroy.argtypes = [c_void_p]
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_num_free.argtypes = [c_void_p]
+    L.pa_bm_num_free.restype = c_int32
+    L.pa_bm_refcount.argtypes = [c_void_p, c_int32]
+    L.pa_bm_refcount.restype = c_int32
+    L.pa_bm_allocate.argtypes = [c_void_p, c_int32, I32P]
+    L.pa_bm_allocate.restype = c_int
+    L.pa_bm_free.argtypes = [c_void_p, I32P, c_int32]
+    L.pa_bm_free.restype = c_int
+    L.pa_bm_fork.argtypes = [c_void_p, I32P, c_int32]
+    L.pa_bm_fork.restype = c_int
+    L.pa_bm_append_slot.argtypes = [c_void_p, I32P, I32P, c_int32, c_int32, I32P, I32P]
+    L.pa_bm_append_slot.restype = c_int
     L.pa_split_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32]
     L.pa_split_workspace_bytes.restype = c_size_t
     L.pa_status_string.argtypes = [c_int]

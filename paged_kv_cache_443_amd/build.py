@@ -26,6 +26,8 @@ SOURCES = [
     "pa_decode_f32.hip",
     "pa_reduce.hip",
     "pa_append.hip",
+    "pa_copy.hip",
+    "pa_block_manager.cpp",
 ]
 
 ARCH = "gfx950"

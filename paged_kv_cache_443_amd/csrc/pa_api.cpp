@@ -153,6 +153,26 @@ pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_se
   return from_hip(pa::launch_reduce(p, stream));
 }
 
+pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs,
+                         hipStream_t stream) {
+  pa_status st = pa::check_copy(cache, block_pairs, num_pairs);
+  if (st != PA_OK || num_pairs == 0) return st;
+  if (static_cast<int64_t>(num_pairs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  static const int32_t kElem[] = {4, 2, 1};  // PA_F32, PA_BF16, PA_I8
+  pa::CopyParams p{};
+  p.k_cache = cache->k_cache;
+  p.v_cache = cache->v_cache;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.pairs = block_pairs;
+  p.num_pairs = num_pairs;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_blocks = cache->num_blocks;
+  p.block_size = cache->block_size;
+  p.tile_bytes = static_cast<size_t>(cache->block_size) * cache->head_dim * kElem[cache->kv_dtype];
+  return from_hip(pa::launch_copy_blocks(p, stream));
+}
+
 size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
   return pa::split_workspace_bytes(num_seqs, num_heads, head_dim, max_num_partitions);
 }
@@ -166,6 +186,8 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_MISALIGNED: return "a pointer is not aligned as required";
     case PA_ERR_BAD_WORKSPACE: return "max_num_partitions too small for max_blocks_per_seq * block_size";
     case PA_ERR_HIP: return "HIP kernel launch failed (see pa_last_hip_error)";
+    case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+    case PA_ERR_INVALID_BLOCK: return "a block id is out of range or not in use";
   }
   return "unknown status";
 }

@@ -66,10 +66,24 @@ struct AppendParams {
   int32_t num_blocks;
 };
 
+struct CopyParams {
+  void *k_cache;
+  void *v_cache;
+  void *k_scale;              // int8 caches only, else null
+  void *v_scale;
+  const int32_t *pairs;       // [num_pairs][2] (source, destination)
+  int32_t num_pairs;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t block_size;
+  size_t tile_bytes;          // one (block, kv head) tile of one pool
+};
+
 // Launchers (one per kernel family); each returns the launch's hipError_t.
 hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
 
 }  // namespace pa
