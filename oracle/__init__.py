@@ -17,6 +17,10 @@ another precision):
   1/sqrt(d), times the cached values); the block-table lookup follows the
   kernel sketch in the same page's PagedAttention question; the GQA head
   map follows page "LLM推理优化", section 1.3.
+* ``decode_multi``: several new query tokens per sequence, each attending
+  causally to the cached tokens up to its own position (the step-t
+  attention applied token by token; chunked prefill, page "vLLM框架是怎么做
+  推理加速的", section 3).
 * ``decode_partials`` / ``merge_partials``: the KV-split form (FlashDecoding,
   page "字节跳动 AI Infra (2)", third question, layer-2 table) -- one
   normalised partial output and log-sum-exp per token range, merged by
@@ -42,6 +46,7 @@ from .paged import (  # noqa: F401
     kv_head_for,
     gather_sequence,
     decode,
+    decode_multi,
     decode_partials,
     merge_partials,
     append,

@@ -90,6 +90,45 @@ def decode(q: np.ndarray, cache: PagedCache, block_tables: np.ndarray, context_l
     return out
 
 
+def decode_multi(q: np.ndarray, q_start: np.ndarray, cache: PagedCache, block_tables: np.ndarray,
+                 context_lens: np.ndarray, scale: float) -> np.ndarray:
+    """Causal attention of several new query tokens per sequence, ``[total, Hq, D]`` (float64).
+
+    Sequence b holds n_b = q_start[b + 1] - q_start[b] new tokens: the last
+    n_b of its L = context_lens[b] cached tokens (their K/V rows already
+    appended).  Query token i of b (row q_start[b] + i) sits at position
+    p = L - n_b + i and attends to the cached tokens t <= p only:
+
+        out[row, h] = sum_{t <= p} exp(s_t - m) v_t / sum_{t <= p} exp(s_t - m),
+        s_t = scale * q[row, h] . k_t.
+
+    This is the step-t attention of page "字节跳动 AI Infra (2)" (KV-cache
+    question) applied to each new token in turn, the shape of a chunked
+    prefill (page "vLLM框架是怎么做推理加速的", section 3) and of verifying
+    draft tokens; n_b = 1 is ``decode``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total, Hq, D = q.shape
+    assert Hq % cache.Hkv == 0 and D == cache.D
+    B = len(context_lens)
+    assert len(q_start) == B + 1 and int(q_start[B]) == total
+    out = np.zeros((total, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        if n > L:
+            raise ValueError("more new tokens than cached tokens")
+        for i in range(n):
+            p = L - n + i
+            for h in range(Hq):
+                K, V = gather_sequence(cache, block_tables[b], p + 1, kv_head_for(h, Hq, cache.Hkv))
+                out[r0 + i, h] = _softmax_apply(_scores(q[r0 + i, h], K, scale), V)[0]
+    return out
+
+
 def decode_partials(q: np.ndarray, cache: PagedCache, block_tables: np.ndarray, context_lens: np.ndarray,
                     scale: float, partition_size: int, max_partitions: int) -> Tuple[np.ndarray, np.ndarray]:
     """KV-split partials: ``part_out [B, Hq, Pmax, D]`` and ``part_lse [B, Hq, Pmax]``.

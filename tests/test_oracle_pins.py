@@ -167,3 +167,49 @@ def test_cow_workload_beams_equal_with_equal_queries():
     assert np.array_equal(w.block_tables[a, :w.shared_blocks[b2]], w.block_tables[b2, :w.shared_blocks[b2]])
     nb = oracle.blocks_for(int(w.context_lens[a]), w.spec.bs)
     assert w.block_tables[a, nb - 1] != w.block_tables[b2, nb - 1]
+
+
+def test_decode_multi_pins():
+    """Causal multi-query decode: one new token is decode; every query row
+    equals decode over the sequence truncated at its own position (computed
+    by the plain definition on a shortened context length); pure-Python
+    brute force agrees on a tiny case; permuting physical blocks changes
+    nothing."""
+    rng = np.random.default_rng(31)
+    Hq, Hkv, D, bs = 4, 2, 16, 4
+    lens = [5, 9, 12, 1]
+    nq = [1, 3, 4, 1]
+    Ks = [pinlib.dyadic(rng, (L, Hkv, D)) for L in lens]
+    Vs = [pinlib.dyadic(rng, (L, Hkv, D)) for L in lens]
+    cache, tb, cl = pinlib.paged_from_dense(Ks, Vs, bs, "f32", rng)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = pinlib.dyadic(rng, (int(qs[-1]), Hq, D))
+    scale = 0.37
+    got = oracle.decode_multi(q, qs, cache, tb, cl, scale)
+    for b, L in enumerate(lens):
+        for i in range(nq[b]):
+            row = qs[b] + i
+            want = oracle.decode(q[row:row + 1], cache, tb[b:b + 1], np.array([L - nq[b] + i + 1]), scale)
+            assert np.max(np.abs(got[row] - want[0])) <= 1e-12
+            if nq[b] == 1:
+                base = oracle.decode(q[row:row + 1], cache, tb[b:b + 1], cl[b:b + 1], scale)
+                assert np.array_equal(got[row], base[0])
+    # pure-Python scalar loops over the flat pool, one truncated context per row
+    rows_q, rows_tb, rows_len = [], [], []
+    for b, L in enumerate(lens):
+        for i in range(nq[b]):
+            rows_q.append(q[qs[b] + i].astype(np.float64).tolist())
+            rows_tb.append(tb[b].tolist())
+            rows_len.append(L - nq[b] + i + 1)
+    brute = oracle.decode_bruteforce([[r[h] for h in range(Hq)] for r in rows_q], cache.k.ravel().tolist(),
+                                     cache.v.ravel().tolist(), None, None, "f32", Hkv, bs, D, rows_tb, rows_len,
+                                     scale)
+    assert np.max(np.abs(got - np.array(brute))) <= 1e-12
+    # causality: changing a key after a row's position does not change that row
+    K2 = [k.copy() for k in Ks]
+    K2[2][-1] += 3.0
+    cache2, tb2, cl2 = pinlib.paged_from_dense(K2, Vs, bs, "f32", np.random.default_rng(99))
+    got2 = oracle.decode_multi(q, qs, cache2, tb2, cl2, scale)
+    last = qs[3] - 1  # the last query row of sequence 2 sees the changed key
+    assert np.max(np.abs(np.delete(got2, last, axis=0) - np.delete(got, last, axis=0))) <= 1e-12
+    assert np.max(np.abs(got2[last] - got[last])) > 1e-6
