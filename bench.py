@@ -232,6 +232,43 @@ def time_copy_blocks(case: Case, steps: int, warmup: int, flush, max_pairs: int 
     return {"pairs": n, "bytes": moved, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}
 
 
+def time_multi(case: Case, steps: int, warmup: int, flush, perfmodel, q_len: int = 4) -> dict:
+    """pa_decode_multi on the workload's cache: q_len new tokens per sequence
+    (a small chunked-prefill chunk, or q_len draft tokens to verify), each
+    attending causally to the cached positions up to its own."""
+    torch, pa, w, s = case.torch, case.pa, case.w, case.s
+    import numpy as np
+    from workloads.device import to_dev_values
+
+    counts = np.minimum(w.context_lens, q_len).astype(np.int32)
+    q_start, q = w.multi_queries(counts)
+    dev = case.q.device
+    qd = to_dev_values(q, s.q_dtype, dev)
+    qs = torch.from_numpy(q_start).to(dev)
+    out = torch.empty(qd.shape, dtype=case.out_dtype, device=dev)
+
+    def run():
+        pa.decode_multi(qd, qs, q_len, case.cache, case.tables, case.lens, s.scale, out)
+
+    for _ in range(warmup):
+        flush()
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs,
+                                   kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
+                                   out_dtype="bf16" if case.out_dtype == torch.bfloat16 else "f32")
+    return {"q_len": q_len, "query_rows": int(counts.sum()), "bytes": nbytes, "us": round(us, 2),
+            "GBps": round(nbytes / us / 1e3, 1), "frac_of_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)}
+
+
 def summarise(case: Case, t: dict, peak: float) -> dict:
     s = case.s
     step_us = t["step"]["mean_us"]
@@ -396,6 +433,8 @@ def main(argv=None) -> int:
     out32 = case.decode_f32().cpu().numpy()
     copy_stats = time_copy_blocks(case, args.steps, args.warmup, flush)
     log(f"copy_blocks: {copy_stats}")
+    multi_stats = time_multi(case, args.steps, args.warmup, flush, perfmodel) if not case.split else {}
+    log(f"decode_multi: {multi_stats}")
 
     s = case.s
     dec_key = "decode_split" if case.split else "decode"
@@ -441,6 +480,7 @@ def main(argv=None) -> int:
         "bytes_per_step": head["bytes"],
         "roofline": roofline,
         "copy_blocks": copy_stats,
+        "decode_multi": multi_stats,
     }
 
     if not args.no_cpu_baseline:

@@ -147,6 +147,41 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
                     void *out, pa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * pa_decode_multi -- paged attention of several new query tokens per
+ * sequence, causally masked (chunked prefill in small chunks, page
+ * "vLLM框架是怎么做推理加速的", section 3; verification of several draft
+ * tokens at once).
+ *
+ * Sequence b has n_b = q_start[b + 1] - q_start[b] new tokens, the last n_b
+ * of its L = context_lens[b] cached tokens (their K/V rows already written
+ * with pa_reshape_and_cache).  Its query token i is row q_start[b] + i of q
+ * and out; it sits at position L - n_b + i and attends to the positions up
+ * to and including its own:
+ *     out[r][h] = sum_{t <= L - n_b + i} softmax_t(scale * q[r][h] . k_t) v_t
+ * (the step-t attention of page "字节跳动 AI Infra (2)", KV-cache question,
+ * taken for each new token in turn).  n_b == 1 for every b is pa_decode,
+ * bit for bit.
+ *
+ *   q             [num_queries][num_heads][head_dim], BF16, 16-byte aligned
+ *   q_start       int32 [num_seqs + 1], non-decreasing, q_start[0] == 0,
+ *                 q_start[num_seqs] == num_queries (device memory)
+ *   num_queries   rows of q and out; <= num_seqs * max_q_len
+ *   max_q_len     an upper bound of every n_b (sets the launch size)
+ *   out           [num_queries][num_heads][head_dim], out_dtype
+ *   other arguments as for pa_decode; the cache must be BF16 or I8
+ *   (F32 returns PA_ERR_UNSUPPORTED).
+ * Preconditions (device data): n_b <= max_q_len and n_b <= L; L as for
+ * pa_decode.  A sequence whose q_start entries leave [0, num_queries], or
+ * with n_b > max_q_len, is skipped (its rows are left as they are); rows of
+ * a sequence with n_b > L are unspecified.  num_seqs == 0 or
+ * num_queries == 0 is a no-op.
+ */
+pa_status pa_decode_multi(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                          const int32_t *q_start, int32_t num_queries, int32_t max_q_len, const pa_kv_cache *cache,
+                          const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          float scale, void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/*
  * pa_decode_split -- first pass of KV-split decode (FlashDecoding: split
  * along the KV length for long sequences; page "字节跳动 AI Infra (2)",
  * third question, layer-2 table).

@@ -23,6 +23,7 @@ __all__ = [
     "KVCache",
     "reshape_and_cache",
     "decode",
+    "decode_multi",
     "decode_split",
     "reduce",
     "split_workspace_bytes",
@@ -165,6 +166,34 @@ def decode(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, context_
                               block_tables.shape[1], _ptr(context_lens), float(scale), _ptr(out), _DT[out.dtype],
                               _stream(q.device))
     _check("pa_decode", st)
+    return out
+
+
+def decode_multi(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, cache: KVCache, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, scale: float, out: torch.Tensor) -> torch.Tensor:
+    """Causal paged attention of several new tokens per sequence.
+
+    ``q`` and ``out`` are ``[num_queries, Hq, D]``; the new tokens of sequence
+    b are rows ``q_start[b] .. q_start[b + 1] - 1`` (int32 ``[B + 1]``, device)
+    and the last of its ``context_lens[b]`` cached positions.  ``max_q_len``
+    bounds every sequence's count of new tokens.  Writes and returns ``out``.
+    """
+    NQ, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("q head_dim differs from the cache's")
+    _need(q, "q", torch.bfloat16)
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    B = block_tables.shape[0]
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(q_start, "q_start", torch.int32, (B + 1,))
+    _need(out, "out", (torch.float32, torch.bfloat16), (NQ, Hq, D))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_decode_multi(_ptr(q), _DT[q.dtype], B, Hq, _ptr(q_start), NQ, int(max_q_len),
+                                    ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1],
+                                    _ptr(context_lens), float(scale), _ptr(out), _DT[out.dtype], _stream(q.device))
+    _check("pa_decode_multi", st)
     return out
 
 

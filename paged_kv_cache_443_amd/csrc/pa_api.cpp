@@ -37,6 +37,10 @@ pa::DecodeParams make_decode_params(const void *q, int32_t num_seqs, int32_t num
   p.num_kv_heads = cache->num_kv_heads;
   p.group = num_heads / cache->num_kv_heads;
   p.head_groups = (p.group + 15) / 16;
+  p.rows_per_group = std::min(16, p.group);
+  p.q_start = nullptr;
+  p.num_queries = num_seqs;
+  p.max_q_len = 1;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = cache->num_blocks;
   p.scale = scale;
@@ -129,6 +133,32 @@ pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int
   p.part_lse = part_lse;
   p.partition_size = partition_size;
   p.max_num_partitions = max_num_partitions;
+  return launch(p, cache, stream);
+}
+
+pa_status pa_decode_multi(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                          const int32_t *q_start, int32_t num_queries, int32_t max_q_len, const pa_kv_cache *cache,
+                          const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          float scale, void *out, pa_dtype out_dtype, hipStream_t stream) {
+  pa_status st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                                         context_lens, scale);
+  if (st != PA_OK) return st;
+  st = pa::check_multi(q_start, num_queries, max_q_len, num_seqs, num_heads, cache);
+  if (st != PA_OK || num_seqs == 0 || num_queries == 0) return st;
+  st = pa::check_out(out, q_dtype, cache->kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  pa::DecodeParams p =
+      make_decode_params(q, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale);
+  const int64_t rows = static_cast<int64_t>(max_q_len) * p.group;  // rows of one (sequence, kv head)
+  p.head_groups = static_cast<int32_t>((rows + 15) / 16);
+  p.rows_per_group = static_cast<int32_t>(std::min<int64_t>(16, rows));
+  p.q_start = q_start;
+  p.num_queries = num_queries;
+  p.max_q_len = max_q_len;
+  p.out = out;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.partition_size = 0;
+  p.max_num_partitions = 1;
   return launch(p, cache, stream);
 }
 

@@ -92,7 +92,9 @@ struct Ctx {
   int32_t num_blocks_m1;
   int32_t kvh;
   int32_t hkv;
-  int32_t t1;
+  int32_t t1;       // end of the token range (positions >= t1 are never used)
+  int32_t t1_row;   // causal multi-query: this lane's query row sees positions < t1_row
+  int32_t t1_min;   // causal multi-query: the smallest t1_row of the unit
   int32_t m, j;
 };
 
@@ -204,7 +206,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return half_bits_to_float
 // Online-softmax update for one chunk; returns the probabilities (V scale
 // folded in for int8) of this lane's tokens TPL*j + e.  TAIL: positions may
 // reach t1.
-template <bool I8, int D, bool TAIL>
+template <bool I8, int D, bool TAIL, bool CAUSAL = false>
 __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, const VBuf<I8, D> &vb, Probs<I8, D> &P,
                                         int tok0, int t1, float scale_log2) {
   using T = Tile<I8, D>;
@@ -229,7 +231,10 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   const float m_new = fmaxf(st.m_run, mloc);
-  const float alpha = fast_exp2(st.m_run - m_new);
+  // a causal query row may see no position of a chunk and nothing before it:
+  // then m_new is -inf and the exponentials below must give 0, not NaN
+  const float m_ref = (CAUSAL && m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m_run - m_ref);
   st.m_run = m_new;
   float psum = 0.f;
 #pragma unroll
@@ -237,7 +242,7 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * q + i;
-      const float pe = fast_exp2(S.s[q][i] - m_new);
+      const float pe = fast_exp2(S.s[q][i] - m_ref);
       psum += pe;
       if constexpr (I8) {
         const uint32_t vw = vb.vs[e >> 3][(e >> 1) & 3];
@@ -331,7 +336,7 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-template <bool I8, int D, int BS, bool TAIL, bool REFILL>
+template <bool I8, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false>
 __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<I8, D> &vb,
                                         const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop, int cs, int cn, Ids idn,
                                         float scale_log2) {
@@ -344,7 +349,7 @@ __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<
     issue_k(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
-  softmax<I8, D, TAIL>(st, S, vb, P, cs + T::TPL * x.j, x.t1, scale_log2);
+  softmax<I8, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2);
   pv_update<I8, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
@@ -355,7 +360,7 @@ __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<
 
 // A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
 // while the previous one is computed.
-template <bool I8, int D, int BS, int NW>
+template <bool I8, int D, int BS, int NW, bool CAUSAL = false>
 __device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
                                                 int c0, int n, float scale_log2) {
   constexpr int STEP = NW * Tile<I8, D>::CT;
@@ -367,10 +372,14 @@ __device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, 
   issue_v(vb, x, cs, ids);
   for (int k = 0; k + 1 < n; ++k) {
     const int cn = cs + STEP;
-    consume<I8, D, BS, false, true>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+    // a causal unit's last new tokens are hidden from its earlier query rows
+    if (CAUSAL && cs + Tile<I8, D>::CT > x.t1_min)
+      consume<I8, D, BS, true, true, CAUSAL>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+    else
+      consume<I8, D, BS, false, true, CAUSAL>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     cs = cn;
   }
-  consume<I8, D, BS, true, false>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
+  consume<I8, D, BS, true, false, CAUSAL>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
 }
 
 // The same with two chunks in flight: buffers A and B alternate; chunk i is in
@@ -415,15 +424,31 @@ __device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, 
 // Every thread of the work-group calls it with the same arguments.  On entry
 // the LDS table window and merge buffers may be reused (the previous unit's
 // readers are past its last barrier); on exit its outputs are written.
-template <bool I8, int D, int BS, int NW, int DEPTH>
+//
+// Query rows.  The (query token, head) pairs a (sequence, kv head) serves are
+// its rows: row r is query token r / G of the sequence with head
+// kv * G + r % G.  A single-token decode has G rows (the GQA group); a causal
+// multi-query unit has n_b * G.  Rows go to the matrix cores 16 at a time:
+// `hx` names a kv head and a group of 16 rows.
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<I8, D>;
+  static_assert(!CAUSAL || DEPTH == 1, "causal rows use the one-deep stream");
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int kvh = hx / p.head_groups;
-  const int g0 = (hx % p.head_groups) * 16;
-  const int gcount = min(16, p.group - g0);
-  const int rows = min(16, p.group);
+  const int r0 = (hx % p.head_groups) * 16;
+  int nq = 1, qbase = b;  // query tokens of the sequence, index of its first one
+  if constexpr (CAUSAL) {
+    qbase = p.q_start[b];
+    nq = p.q_start[b + 1] - qbase;
+  }
+  const int nrows = nq * p.group;
+  // no row of this group, or q_start out of its stated bounds: uniform over
+  // the work-group, before any barrier
+  if (CAUSAL && (r0 >= nrows || qbase < 0 || qbase + nq > p.num_queries || nq > p.max_q_len)) return;
+  const int gcount = min(16, nrows - r0);
+  const int rows = p.rows_per_group;
   const int TW = p.tbl_window;
   const bool split = p.partition_size > 0;
 
@@ -454,12 +479,19 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm.tbl;
 
-  // ---- query operand (B of the QK product): head m of the group -----------
+  // ---- query operand (B of the QK product): row r0 + m -------------------------
   QOp<I8, D> qop;
   {
+    const int r = r0 + x.m;
+    const int qi = CAUSAL ? r / p.group : 0;  // single-token rows are heads of query token 0
     const bool qvalid = x.m < gcount;
-    const int hq = kvh * p.group + g0 + x.m;
-    const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(b) * p.num_heads + hq) * D;
+    const int hq = kvh * p.group + (CAUSAL ? r % p.group : r);
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(qbase + qi) * p.num_heads + hq) * D;
+    // causal rows: query token qi sits at position L - nq + qi and sees the
+    // positions up to it (rows past the group's last one see all L)
+    x.t1_row = min(L - nq + qi + 1, L);
+    x.t1_min = L - nq + 1;
 #pragma unroll
     for (int s = 0; s < T::NS; ++s) {
       const int d0 = I8 ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
@@ -495,7 +527,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int n = w < nch ? (nch - w + NW - 1) / NW : 0;
     if (n > 0) {
       if constexpr (DEPTH == 1)
-        stream_chunks_1<I8, D, BS, NW>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
+        stream_chunks_1<I8, D, BS, NW, CAUSAL>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
       else
         stream_chunks_2<I8, D, BS, NW>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
     }
@@ -534,8 +566,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
       o = osum / lsum;
       lse = (M + __log2f(lsum)) * kLn2;
     }
-    const int hq = kvh * p.group + g0 + gi;
-    const size_t row = static_cast<size_t>(b) * p.num_heads + hq;
+    const int r = r0 + gi;
+    const int qi = CAUSAL ? r / p.group : 0;
+    const int hq = kvh * p.group + (CAUSAL ? r % p.group : r);
+    const size_t row = static_cast<size_t>(qbase + qi) * p.num_heads + hq;
     if (split) {
       const size_t prow = row * p.max_num_partitions + part;
       p.part_out[prow * D + d] = o;
@@ -555,10 +589,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <bool I8, int D, int BS, int NW, int DEPTH>
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
+  const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
   const int HX = p.num_kv_heads * p.head_groups;
   const int nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int id = blockIdx.x;
@@ -598,7 +632,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<I8, D, BS, NW, DEPTH>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<I8, D, BS, NW, DEPTH, CAUSAL>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -612,7 +646,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 template <bool I8, int D, int BS, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const Smem sm = carve<D, NW>(smem, p.tbl_window, min(16, p.group));
+  const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
   const int HX = p.num_kv_heads * p.head_groups;
   const int B = p.num_seqs;
   const int Lmax = p.max_blocks_per_seq * BS;
@@ -670,7 +704,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
 // else one work-group per (unit, partition).
 template <bool I8, int D, int BS, int NW, int DEPTH>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
-  const int rows = min(16, p.group);
+  const int rows = p.rows_per_group;
   if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
     const auto kern = decode_split_persistent_kernel<I8, D, BS, NW, DEPTH>;
@@ -697,14 +731,14 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
 // than one work-group, so that another one streams while a work-group ranks
 // (measured: +3 points for four-wave int8 units; with one eight-wave
 // work-group per CU the ranking is dead time and cost 2 points).
-template <bool I8, int D, int BS, int NW, int DEPTH>
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
 hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
-  p.lpt = (NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
+  p.lpt = (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
-  const size_t lds = lds_bytes<D, NW>(p.tbl_window, min(16, p.group), p.lpt ? p.num_seqs + 1 : 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
-                     lds, s, p);
+  const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH, CAUSAL>), dim3(static_cast<uint32_t>(nwg)),
+                     dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
 
@@ -716,11 +750,14 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
 // measured faster.
 template <bool I8, int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
+  const bool causal = p.q_start != nullptr;
   if constexpr (I8) {
     if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
+    if (causal) return launch_single<I8, D, BS, 4, 1, true>(p, s);
     return launch_single<I8, D, BS, 4, 1>(p, s);
   } else {
     if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
+    if (causal) return launch_single<I8, D, BS, 8, 1, true>(p, s);
     return launch_single<I8, D, BS, 8, 1>(p, s);
   }
 }

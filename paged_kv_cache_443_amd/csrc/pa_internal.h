@@ -26,7 +26,11 @@ struct DecodeParams {
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;              // num_heads / num_kv_heads
-  int32_t head_groups;        // ceil(group / 16): query-head groups of <= 16 per work-group
+  int32_t head_groups;        // groups of <= 16 query rows per kv head: ceil(max query tokens * group / 16)
+  int32_t rows_per_group;     // min(16, max query tokens * group): LDS rows of a work-group
+  const int32_t *q_start;     // causal multi-query: [num_seqs + 1] first query row of each sequence, else null
+  int32_t num_queries;        // causal multi-query: rows of q and out
+  int32_t max_q_len;          // causal multi-query: bound of any sequence's query tokens
   int32_t max_blocks_per_seq;
   int32_t num_blocks;
   int32_t partition_size;     // 0: whole sequence (pa_decode)

@@ -82,6 +82,23 @@ pa_status check_split(int32_t partition_size, int32_t max_num_partitions, int32_
   return PA_OK;
 }
 
+pa_status check_multi(const int32_t *q_start, int32_t num_queries, int32_t max_q_len, int32_t num_seqs,
+                      int32_t num_heads, const pa_kv_cache *cache) {
+  // the matrix-core path only: a bf16 or int8 cache
+  if (cache->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (num_queries < 0 || max_q_len < 1) return PA_ERR_BAD_SHAPE;
+  // every sequence's query rows fit max_q_len, so the rows of all fit the bound
+  if (static_cast<int64_t>(num_queries) > static_cast<int64_t>(num_seqs) * max_q_len) return PA_ERR_BAD_SHAPE;
+  // rows (query token x head) of one kv head, and rows of q, in 32 bits
+  const int64_t group = num_heads / cache->num_kv_heads;
+  if (static_cast<int64_t>(max_q_len) * group + 15 > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(num_queries) * num_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || num_queries == 0) return PA_OK;
+  if (q_start == nullptr) return PA_ERR_NULL_PTR;
+  if (!aligned(q_start, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
 pa_status check_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
                        int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
                        int32_t partition_size, const void *out, pa_dtype out_dtype) {

@@ -18,6 +18,8 @@ pa_status check_decode_common(const void *q, pa_dtype q_dtype, int32_t num_seqs,
 pa_status check_out(const void *out, pa_dtype q_dtype, pa_dtype kv_dtype, pa_dtype out_dtype);
 pa_status check_split(int32_t partition_size, int32_t max_num_partitions, int32_t block_size,
                       int32_t max_blocks_per_seq, const float *part_out, const float *part_lse);
+pa_status check_multi(const int32_t *q_start, int32_t num_queries, int32_t max_q_len, int32_t num_seqs,
+                      int32_t num_heads, const pa_kv_cache *cache);
 pa_status check_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
                        int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
                        int32_t partition_size, const void *out, pa_dtype out_dtype);

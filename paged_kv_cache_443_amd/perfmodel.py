@@ -46,6 +46,24 @@ def decode_bytes(context_lens: Iterable[int], *, Hq: int, Hkv: int, D: int, bs: 
     return int(kv + qo + tables)
 
 
+def multi_bytes(context_lens: Iterable[int], query_counts: Iterable[int], *, Hq: int, Hkv: int, D: int, bs: int,
+                kv_dtype: str, q_dtype: str, out_dtype: str) -> int:
+    """Bytes one causal multi-query launch must move: every cached K/V row
+    once, the query and output rows of every new token, the tables and the
+    row offsets."""
+    L = np.asarray(list(context_lens), dtype=np.int64)
+    n = np.asarray(list(query_counts), dtype=np.int64)
+    rows = int(n.sum())
+    e = ELEM_BYTES[kv_dtype]
+    toks = int(L.sum())
+    kv = toks * Hkv * D * 2 * e
+    if kv_dtype == "i8":
+        kv += toks * Hkv * 2 * 2
+    qo = rows * Hq * D * (ELEM_BYTES[q_dtype] + ELEM_BYTES[out_dtype])
+    tables = int(np.sum((L + bs - 1) // bs)) * 4 + len(L) * 4 + (len(L) + 1) * 4
+    return int(kv + qo + tables)
+
+
 def append_bytes(num_tokens: int, *, Hkv: int, D: int, kv_dtype: str, src_dtype: str) -> int:
     """Bytes one cache append moves: source rows read, cache rows (+ scales) written, slots read."""
     T = int(num_tokens)

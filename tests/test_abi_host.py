@@ -92,6 +92,30 @@ def test_decode_rejections(L):
     assert L.pa_decode(None, PA_BF16, 0, 8, ctypes.byref(c), None, 8, None, 0.1, None, PA_F32, None) == PA_OK
 
 
+def _multi(L, cache, qs=A16[10], nq=6, mq=3, B=4, Hq=8, q=A16[4], out=A16[7], odt=PA_F32):
+    return L.pa_decode_multi(q, PA_BF16, B, Hq, qs, nq, mq, ctypes.byref(cache), A16[5], 8, A16[6], 0.1, out, odt,
+                             None)
+
+
+def test_multi_rejections(L):
+    c = _cache()
+    assert _multi(L, c, qs=None) == PA_ERR_NULL_PTR
+    assert _multi(L, c, q=None) == PA_ERR_NULL_PTR
+    assert _multi(L, c, out=None) == PA_ERR_NULL_PTR
+    assert _multi(L, _cache(kv=PA_F32)) == PA_ERR_UNSUPPORTED  # matrix-core caches only
+    assert _multi(L, c, mq=0) == PA_ERR_BAD_SHAPE
+    assert _multi(L, c, nq=-1) == PA_ERR_BAD_SHAPE
+    assert _multi(L, c, nq=13, mq=3) == PA_ERR_BAD_SHAPE  # more rows than num_seqs * max_q_len
+    assert _multi(L, c, mq=2 ** 30, nq=6) == PA_ERR_BAD_SHAPE  # rows per kv head overflow int32
+    assert _multi(L, c, qs=A16[10] + 2) == PA_ERR_MISALIGNED
+    assert _multi(L, c, odt=PA_I8) == PA_ERR_UNSUPPORTED
+    assert _multi(L, c, Hq=7) == PA_ERR_BAD_SHAPE
+    # no rows, or no sequences: a no-op that never touches the (null) pointers
+    assert _multi(L, c, nq=0, qs=None, out=None) == PA_OK
+    assert L.pa_decode_multi(None, PA_BF16, 0, 8, None, 0, 1, ctypes.byref(c), None, 8, None, 0.1, None, PA_F32,
+                             None) == PA_OK
+
+
 def _split(L, cache, P=512, Pmax=1, po=A16[8], pl=A16[9], mbps=8, B=4):
     return L.pa_decode_split(A16[4], PA_BF16, B, 8, ctypes.byref(cache), A16[5], mbps, A16[6], 0.1, P, Pmax, po, pl,
                              None)

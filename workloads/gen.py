@@ -234,6 +234,28 @@ class Workload:
             sl[b] = self.slots(b, L - 1, L)[0]
         return Kn, Vn, sl
 
+    def query_counts(self, max_q: int) -> np.ndarray:
+        """New tokens per sequence for a multi-query step: uniform in
+        [1, min(max_q, L)] (0 for an empty sequence), seeded."""
+        rng = self._rng(3)
+        hi = np.minimum(self.context_lens.astype(np.int64), int(max_q))
+        n = rng.integers(1, np.maximum(hi, 1) + 1)
+        return np.where(hi > 0, n, 0).astype(np.int32)
+
+    def multi_queries(self, counts: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        """Queries of a multi-query step: ``q_start [B + 1]`` (int32, the
+        exclusive prefix sum of ``counts``) and ``q [total, Hq, D]`` (float32
+        values exact in the q dtype), standard normal like ``q``."""
+        s = self.spec
+        counts = np.asarray(counts, np.int64)
+        assert counts.shape == (s.B,) and np.all(counts >= 0)
+        q_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        rng = self._rng(4)
+        q = rng.standard_normal((int(q_start[-1]), s.Hq, s.D), dtype=np.float32)
+        if s.q_dtype == "bf16":
+            q = bf16_round(q)
+        return q_start, q
+
     def used_blocks(self) -> np.ndarray:
         """Distinct physical blocks referenced by the valid table entries."""
         ids = [self.block_tables[b, : blocks_needed(int(L), self.spec.bs)] for b, L in enumerate(self.context_lens)]
