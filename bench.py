@@ -58,6 +58,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="upper bound on the oracle's timed CPU work")
+    ap.add_argument("--no-multi-shapes", action="store_true",
+                    help="skip the extra multi-query shapes (verification and chunked-prefill sizes)")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (calibrates rocprofv3 byte counters)")
@@ -267,6 +269,59 @@ def time_multi(case: Case, steps: int, warmup: int, flush, perfmodel, q_len: int
                                    out_dtype="bf16" if case.out_dtype == torch.bfloat16 else "f32")
     return {"q_len": q_len, "query_rows": int(counts.sum()), "bytes": nbytes, "us": round(us, 2),
             "GBps": round(nbytes / us / 1e3, 1), "frac_of_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)}
+
+
+# multi-query shapes beyond the headline workload's 4-token step: (name, heads,
+# kv heads, cached tokens per sequence, new tokens per sequence, sequences)
+MULTI_SHAPES = [
+    ("gqa70b-verify8", 64, 8, 2048, 8, 32),      # 8 draft tokens to verify, 70B-shaped heads
+    ("mha13b-chunk512", 40, 40, 2048, 512, 8),   # 512-token chunked-prefill chunks, 13B-shaped heads
+    ("gqa70b-chunk512", 64, 8, 2048, 512, 8),
+]
+
+
+def time_multi_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush) -> dict:
+    """pa_decode_multi on a synthetic cache of its own (bf16, D 128, bs 16)."""
+    import numpy as np
+    from workloads import make_custom
+    from workloads.device import append_tokens, meta, to_dev_values
+
+    name, Hq, Hkv, L, n, B = shape
+    w = make_custom(B=B, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype="bf16", lengths=[L] * B, seed=11)
+    dev = torch.device("cuda:0")
+    cache = pa.KVCache.allocate(w.num_blocks, Hkv, 16, 128, "bf16", dev)
+    append_tokens(w, cache)
+    counts = np.full(B, n, np.int32)
+    q_start, q = w.multi_queries(counts)
+    _, tables, lens = meta(w)
+    qd = to_dev_values(q, "bf16")
+    qs = torch.from_numpy(q_start).to(dev)
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        pa.decode_multi(qd, qs, n, cache, tables, lens, w.spec.scale, out)
+
+    for _ in range(warmup):
+        flush()
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype="bf16",
+                                   q_dtype="bf16", out_dtype="bf16")
+    flops = perfmodel.multi_flops(w.context_lens, counts, Hq=Hq, D=128)
+    del cache, qd, out
+    torch.cuda.empty_cache()
+    return {"q_len": n, "batch": B, "cached_tokens": L, "q_heads": Hq, "kv_heads": Hkv, "us": round(us, 2),
+            "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4),
+            "TFLOPs": round(flops / us / 1e6, 1),
+            "frac_of_mfma_peak": round(flops / us / 1e6 / perfmodel.MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def summarise(case: Case, t: dict, peak: float) -> dict:
@@ -488,6 +543,13 @@ def main(argv=None) -> int:
     case.free()
     del case
     torch.cuda.empty_cache()
+
+    if not args.no_multi_shapes:
+        shapes = {}
+        for shape in MULTI_SHAPES:
+            shapes[shape[0]] = time_multi_shape(torch, pa, perfmodel, shape, args.steps, args.warmup, flush)
+            log(f"decode_multi {shape[0]}: {shapes[shape[0]]}")
+        multi_stats["shapes"] = shapes
 
     other = {}
     for c in others:

@@ -125,7 +125,10 @@ __device__ __forceinline__ Ids read_ids(const Ctx<I8, D, BS> &x, int cs) {
   return r;
 }
 
-template <bool I8, int D, int BS>
+// NT: non-temporal loads where they pay (every unit reads its K/V once);
+// ordinary loads when several row groups of a unit read the same lines, so
+// that the later reads hit the cache.
+template <bool NT, bool I8, int D, int BS>
 __device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
   using T = Tile<I8, D>;
   const size_t ktile = static_cast<size_t>(static_cast<uint32_t>(id.k) * static_cast<uint32_t>(x.hkv) + x.kvh);
@@ -136,11 +139,11 @@ __device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x
     const int off = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
     const int ok = I8 ? off : bf16_k_slot(off);  // lanes m % 8 read one 128-byte run
 #pragma unroll
-    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_tile<!I8>(kp + (4 * s + x.j) * BS + ok);
+    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_tile<NT && !I8>(kp + (4 * s + x.j) * BS + ok);
   }
 }
 
-template <bool I8, int D, int BS>
+template <bool NT, bool I8, int D, int BS>
 __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
   using T = Tile<I8, D>;
   const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
@@ -156,7 +159,7 @@ __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x
   }
   const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<true>(vp + 16 * n);
+  for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<NT>(vp + 16 * n);
 }
 
 template <bool I8, int D>
@@ -336,7 +339,7 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-template <bool I8, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false>
+template <bool I8, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true>
 __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<I8, D> &vb,
                                         const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop, int cs, int cn, Ids idn,
                                         float scale_log2) {
@@ -346,21 +349,21 @@ __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<
   qk<I8, D>(S, kb, qop);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_k(kb, x, cn, idn);
+    issue_k<NT>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax<I8, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2);
   pv_update<I8, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_v(vb, x, cn, idn);
+    issue_v<NT>(vb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
 // while the previous one is computed.
-template <bool I8, int D, int BS, int NW, bool CAUSAL = false>
+template <bool I8, int D, int BS, int NW, bool CAUSAL = false, bool NT = true>
 __device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
                                                 int c0, int n, float scale_log2) {
   constexpr int STEP = NW * Tile<I8, D>::CT;
@@ -368,18 +371,18 @@ __device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, 
   VBuf<I8, D> vb;
   int cs = c0;
   const Ids ids = read_ids(x, cs);
-  issue_k(kb, x, cs, ids);
-  issue_v(vb, x, cs, ids);
+  issue_k<NT>(kb, x, cs, ids);
+  issue_v<NT>(vb, x, cs, ids);
   for (int k = 0; k + 1 < n; ++k) {
     const int cn = cs + STEP;
     // a causal unit's last new tokens are hidden from its earlier query rows
     if (CAUSAL && cs + Tile<I8, D>::CT > x.t1_min)
-      consume<I8, D, BS, true, true, CAUSAL>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+      consume<I8, D, BS, true, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     else
-      consume<I8, D, BS, false, true, CAUSAL>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+      consume<I8, D, BS, false, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     cs = cn;
   }
-  consume<I8, D, BS, true, false, CAUSAL>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
+  consume<I8, D, BS, true, false, CAUSAL, NT>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
 }
 
 // The same with two chunks in flight: buffers A and B alternate; chunk i is in
@@ -392,12 +395,12 @@ __device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, 
   VBuf<I8, D> va, vb;
   {
     const Ids i0 = read_ids(x, c0);
-    issue_k(ka, x, c0, i0);
-    issue_v(va, x, c0, i0);
+    issue_k<true>(ka, x, c0, i0);
+    issue_v<true>(va, x, c0, i0);
     if (n > 1) {
       const Ids i1 = read_ids(x, c0 + STEP);
-      issue_k(kb, x, c0 + STEP, i1);
-      issue_v(vb, x, c0 + STEP, i1);
+      issue_k<true>(kb, x, c0 + STEP, i1);
+      issue_v<true>(vb, x, c0 + STEP, i1);
     }
   }
   int i = 0;
@@ -428,26 +431,36 @@ __device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, 
 // Query rows.  The (query token, head) pairs a (sequence, kv head) serves are
 // its rows: row r is query token r / G of the sequence with head
 // kv * G + r % G.  A single-token decode has G rows (the GQA group); a causal
-// multi-query unit has n_b * G.  Rows go to the matrix cores 16 at a time:
-// `hx` names a kv head and a group of 16 rows.
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
+// multi-query unit has n_b * G.  Rows go to the matrix cores 16 at a time (a
+// row group).  A unit takes R consecutive row groups of one kv head (`hx`
+// names the kv head and the unit's first group / R): wavefront w serves row
+// group w % R and takes every (NW / R)-th chunk of that group's tokens, so
+// the R groups walk the same K/V chunks at about the same time and all but
+// the first read of each line come from the cache.
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<I8, D>;
   static_assert(!CAUSAL || DEPTH == 1, "causal rows use the one-deep stream");
+  static_assert(R == 1 || CAUSAL, "several row groups per unit only for multi-query units");
+  static_assert(NW % R == 0, "row groups must divide the wavefronts");
+  constexpr int NWT = NW / R;  // wavefronts sharing one row group's tokens
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int wr = R == 1 ? 0 : w % R;
+  const int wt = R == 1 ? w : w / R;
   const int kvh = hx / p.head_groups;
-  const int r0 = (hx % p.head_groups) * 16;
+  const int rg0 = (hx % p.head_groups) * R;  // the unit's first row group
+  const int r0 = (rg0 + wr) * 16;            // this wavefront's first row
   int nq = 1, qbase = b;  // query tokens of the sequence, index of its first one
   if constexpr (CAUSAL) {
     qbase = p.q_start[b];
     nq = p.q_start[b + 1] - qbase;
   }
   const int nrows = nq * p.group;
-  // no row of this group, or q_start out of its stated bounds: uniform over
-  // the work-group, before any barrier
-  if (CAUSAL && (r0 >= nrows || qbase < 0 || qbase + nq > p.num_queries || nq > p.max_q_len)) return;
-  const int gcount = min(16, nrows - r0);
+  // no row in the unit, or q_start out of its stated bounds: uniform over the
+  // work-group, before any barrier
+  if (CAUSAL && (rg0 * 16 >= nrows || qbase < 0 || qbase + nq > p.num_queries || nq > p.max_q_len)) return;
+  const int gcount = min(16, nrows - r0);  // rows of this wavefront's group (<= 0: none)
   const int rows = p.rows_per_group;
   const int TW = p.tbl_window;
   const bool split = p.partition_size > 0;
@@ -479,6 +492,18 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm.tbl;
 
+  // end of the positions read: a causal group's last row sees nothing past
+  // its own position (none at all when nq > L: t1 <= 0).  x.t1 is this
+  // wavefront's end, t1u the unit's (its last row group's).
+  x.t1 = split ? min(t0 + p.partition_size, L) : L;
+  int t1u = x.t1;
+  if constexpr (CAUSAL) {
+    const int r_last = min(nrows, (rg0 + R) * 16) - 1;
+    t1u = min(x.t1, L - nq + r_last / p.group + 1);
+    x.t1 = gcount > 0 ? min(x.t1, L - nq + (r0 + gcount - 1) / p.group + 1) : t0;
+  }
+  x.nbv = (x.t1 + BS - 1) / BS;
+
   // ---- query operand (B of the QK product): row r0 + m -------------------------
   QOp<I8, D> qop;
   {
@@ -489,9 +514,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const uint16_t *qrow =
         static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(qbase + qi) * p.num_heads + hq) * D;
     // causal rows: query token qi sits at position L - nq + qi and sees the
-    // positions up to it (rows past the group's last one see all L)
-    x.t1_row = min(L - nq + qi + 1, L);
-    x.t1_min = L - nq + 1;
+    // positions up to it (lanes past the group's last row: up to t1); chunks
+    // wholly before the group's first row's position need no mask
+    x.t1_row = min(L - nq + qi + 1, x.t1);
+    x.t1_min = L - nq + r0 / p.group + 1;
 #pragma unroll
     for (int s = 0; s < T::NS; ++s) {
       const int d0 = I8 ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
@@ -501,9 +527,6 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     }
   }
 
-  x.t1 = split ? min(t0 + p.partition_size, L) : L;
-  x.nbv = (x.t1 + BS - 1) / BS;
-
   State<I8, D> st;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -512,8 +535,8 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   __syncthreads();  // first table window staged
 
   // ---- token range in windows of staged block-table entries (usually one) ----
-  for (int ws = t0; ws < x.t1; ws += TW * BS) {
-    const int we = min(ws + TW * BS, x.t1);
+  for (int ws = t0; ws < t1u; ws += TW * BS) {
+    const int we = min(ws + TW * BS, t1u);
     x.lb0 = ws / BS;
     if (ws != t0) {
       const int nbw = (we + BS - 1) / BS - x.lb0;
@@ -522,14 +545,16 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
       __syncthreads();
     }
 
-    // chunks ws + c*CT of this window; wave w takes c = w, w + NW, ...
-    const int nch = (we - ws + T::CT - 1) / T::CT;
-    const int n = w < nch ? (nch - w + NW - 1) / NW : 0;
+    // chunks ws + c*CT of this window below this wavefront's end; token share
+    // wt takes c = wt, wt + NWT, ...
+    const int wew = R == 1 ? we : min(we, x.t1);
+    const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
+    const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
     if (n > 0) {
       if constexpr (DEPTH == 1)
-        stream_chunks_1<I8, D, BS, NW, CAUSAL>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
+        stream_chunks_1<I8, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
       else
-        stream_chunks_2<I8, D, BS, NW>(st, x, qop, ws + w * T::CT, n, p.scale_log2);
+        stream_chunks_2<I8, D, BS, NWT>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
     }
   }
 
@@ -547,37 +572,44 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
   __syncthreads();
 
-  for (int e = threadIdx.x; e < gcount * D; e += NW * 64) {
-    const int gi = e / D;
-    const int d = e % D;
-    float M = -INFINITY;
+  // row group `slot` of the unit: states of wavefronts slot, slot + R, ...
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm.m[v * rows + gi]);
-    float o = 0.f;
-    float lse = -INFINITY;
-    if (M != -INFINITY) {
-      float lsum = 0.f, osum = 0.f;
+  for (int slot = 0; slot < R; ++slot) {
+    const int rs0 = (rg0 + slot) * 16;
+    const int gc = R == 1 ? gcount : min(16, nrows - rs0);
+    for (int e = threadIdx.x; e < gc * D; e += NW * 64) {
+      const int gi = e / D;
+      const int d = e % D;
+      float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        const float f = fast_exp2(sm.m[v * rows + gi] - M);
-        lsum += f * sm.l[v * rows + gi];
-        osum += f * sm.acc[(static_cast<size_t>(v) * rows + gi) * (D + 4) + d];
+      for (int t = 0; t < NWT; ++t) M = fmaxf(M, sm.m[(slot + t * R) * rows + gi]);
+      float o = 0.f;
+      float lse = -INFINITY;
+      if (M != -INFINITY) {
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NWT; ++t) {
+          const int v = slot + t * R;
+          const float f = fast_exp2(sm.m[v * rows + gi] - M);
+          lsum += f * sm.l[v * rows + gi];
+          osum += f * sm.acc[(static_cast<size_t>(v) * rows + gi) * (D + 4) + d];
+        }
+        o = osum / lsum;
+        lse = (M + __log2f(lsum)) * kLn2;
       }
-      o = osum / lsum;
-      lse = (M + __log2f(lsum)) * kLn2;
-    }
-    const int r = r0 + gi;
-    const int qi = CAUSAL ? r / p.group : 0;
-    const int hq = kvh * p.group + (CAUSAL ? r % p.group : r);
-    const size_t row = static_cast<size_t>(qbase + qi) * p.num_heads + hq;
-    if (split) {
-      const size_t prow = row * p.max_num_partitions + part;
-      p.part_out[prow * D + d] = o;
-      if (d == 0) p.part_lse[prow] = lse;
-    } else if (p.out_bf16) {
-      static_cast<uint16_t *>(p.out)[row * D + d] = float_to_bf16_bits(o);
-    } else {
-      static_cast<float *>(p.out)[row * D + d] = o;
+      const int r = rs0 + gi;
+      const int qi = CAUSAL ? r / p.group : 0;
+      const int hq = kvh * p.group + (CAUSAL ? r % p.group : r);
+      const size_t row = static_cast<size_t>(qbase + qi) * p.num_heads + hq;
+      if (split) {
+        const size_t prow = row * p.max_num_partitions + part;
+        p.part_out[prow * D + d] = o;
+        if (d == 0) p.part_lse[prow] = lse;
+      } else if (p.out_bf16) {
+        static_cast<uint16_t *>(p.out)[row * D + d] = float_to_bf16_bits(o);
+      } else {
+        static_cast<float *>(p.out)[row * D + d] = o;
+      }
     }
   }
 }
@@ -589,7 +621,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -632,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<I8, D, BS, NW, DEPTH, CAUSAL>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<I8, D, BS, NW, DEPTH, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -731,15 +763,27 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
 // than one work-group, so that another one streams while a work-group ranks
 // (measured: +3 points for four-wave int8 units; with one eight-wave
 // work-group per CU the ranking is dead time and cost 2 points).
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false>
+template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
 hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
   p.lpt = (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
+  p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH, CAUSAL>), dim3(static_cast<uint32_t>(nwg)),
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
                      dim3(NW * 64), lds, s, p);
   return hipGetLastError();
+}
+
+// Causal multi-query: R = row groups per unit, the smallest power of two that
+// covers a sequence's row groups, at most the wavefront count.
+template <bool I8, int D, int BS, int NW>
+hipError_t launch_causal(const DecodeParams &p, hipStream_t s) {
+  const int rg = p.head_groups;  // row groups of a (sequence, kv head)
+  if (rg <= 1) return launch_single<I8, D, BS, NW, 1, true, 1>(p, s);
+  if (rg <= 2) return launch_single<I8, D, BS, NW, 1, true, 2>(p, s);
+  if (rg <= 4 || NW == 4) return launch_single<I8, D, BS, NW, 1, true, 4>(p, s);
+  return launch_single<I8, D, BS, NW, 1, true, (NW >= 8 ? 8 : 4)>(p, s);
 }
 
 // Wavefronts per unit.  A single-pass bf16 unit is a whole sequence: eight
@@ -753,11 +797,11 @@ hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
   const bool causal = p.q_start != nullptr;
   if constexpr (I8) {
     if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
-    if (causal) return launch_single<I8, D, BS, 4, 1, true>(p, s);
+    if (causal) return launch_causal<I8, D, BS, 4>(p, s);
     return launch_single<I8, D, BS, 4, 1>(p, s);
   } else {
     if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
-    if (causal) return launch_single<I8, D, BS, 8, 1, true>(p, s);
+    if (causal) return launch_causal<I8, D, BS, 8>(p, s);
     return launch_single<I8, D, BS, 8, 1>(p, s);
   }
 }

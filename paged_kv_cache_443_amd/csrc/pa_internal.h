@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t group;              // num_heads / num_kv_heads
   int32_t head_groups;        // groups of <= 16 query rows per kv head: ceil(max query tokens * group / 16)
+                              // (the causal launcher packs R of them per unit and stores ceil(groups / R))
   int32_t rows_per_group;     // min(16, max query tokens * group): LDS rows of a work-group
   const int32_t *q_start;     // causal multi-query: [num_seqs + 1] first query row of each sequence, else null
   int32_t num_queries;        // causal multi-query: rows of q and out

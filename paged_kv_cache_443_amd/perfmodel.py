@@ -14,6 +14,7 @@ import numpy as np
 
 ELEM_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, vendor figure (no sparsity)
 
 
 def kv_cache_bytes_per_sequence(layers: int, heads: int, seq_len: int, head_dim: int, dtype_bytes: int) -> int:
@@ -62,6 +63,17 @@ def multi_bytes(context_lens: Iterable[int], query_counts: Iterable[int], *, Hq:
     qo = rows * Hq * D * (ELEM_BYTES[q_dtype] + ELEM_BYTES[out_dtype])
     tables = int(np.sum((L + bs - 1) // bs)) * 4 + len(L) * 4 + (len(L) + 1) * 4
     return int(kv + qo + tables)
+
+
+def multi_flops(context_lens: Iterable[int], query_counts: Iterable[int], *, Hq: int, D: int) -> int:
+    """Flops of causal multi-query attention: 2·D for q·k plus 2·D for p·v
+    per (query row, head, visible position); query token i of a sequence
+    with n new tokens and L cached ones sees L - n + i + 1 positions."""
+    total = 0
+    for L, n in zip(context_lens, query_counts):
+        L, n = int(L), int(n)
+        total += n * (L - n) + n * (n + 1) // 2  # sum of L - n + i + 1 over i < n
+    return int(4 * D * Hq * total)
 
 
 def append_bytes(num_tokens: int, *, Hkv: int, D: int, kv_dtype: str, src_dtype: str) -> int:
