@@ -35,6 +35,11 @@ another precision):
   pool (page "字节跳动 AI Infra (2)", PagedAttention question, block-pool
   figure; page "LLM推理优化", section 3.2).
 
+* ``swap_blocks``: whole blocks moved between a GPU pool and a host pool of
+  the same layout, for preemption (page "字节跳动 AI Infra (2)",
+  PagedAttention question, scheduling list; page "vLLM框架是怎么做推理加速的",
+  section 2 and its second follow-up).
+
 Parity status: every function here is pinned by tests that do not re-use
 its own code path (closed forms, invariants, pure-Python brute force, the
 pages' worked block counts); see ``tests/test_oracle_pins.py``.
@@ -53,4 +58,4 @@ from .paged import (  # noqa: F401
     build_cache,
 )
 from .brute import decode_bruteforce  # noqa: F401
-from .blocks import BlockManager, OutOfBlocks, copy_blocks  # noqa: F401
+from .blocks import BlockManager, OutOfBlocks, copy_blocks, swap_blocks  # noqa: F401

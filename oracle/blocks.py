@@ -18,9 +18,22 @@ TEST INFRASTRUCTURE (see ``oracle/__init__``).
   a token into a block that another sequence also references, the block is
   copied into a fresh one that only the writer references (copy-on-write).
 
+* ``swap_blocks``: the same whole-block copy between two pools of one
+  layout, a GPU pool and a host pool.  When GPU memory runs short, or a
+  request is preempted, its KV cache is moved to CPU memory and brought back
+  before it runs again (page "字节跳动 AI Infra (2)", PagedAttention question,
+  scheduling list, and the preemption/swap row of the third question's
+  layer-4 table; page "vLLM框架是怎么做推理加速的", section 2 (swapped queue,
+  long requests swapped out to CPU) and its second follow-up (a swap costs
+  10-20 ms)).  A block's contents are the same wherever it lives, so a
+  sequence swapped out and back in under new block ids decodes exactly as
+  before.
+
 Readings where the pages are silent: free blocks are handed out lowest id
 first; a fork shares the parent's blocks (no copy happens until a write); a
-write into a shared block copies that block only.
+write into a shared block copies that block only; a swap copies whole blocks
+(every kv head, and the scales of an int8 cache) between pools of the same
+layout, and its block ids are independent in the two pools.
 """
 from __future__ import annotations
 
@@ -57,6 +70,35 @@ def copy_blocks(cache: PagedCache, pairs: Sequence[Tuple[int, int]]) -> None:
         if before_ks is not None:
             cache.k_scale[d] = before_ks[s]
             cache.v_scale[d] = before_vs[s]
+
+
+def swap_blocks(src: PagedCache, dst: PagedCache, pairs: Sequence[Tuple[int, int]]) -> None:
+    """Copy block ``s`` of pool ``src`` to block ``d`` of pool ``dst`` for every
+    (s, d) in ``pairs`` (swap out: GPU pool -> host pool; swap in: the reverse).
+
+    Preconditions (checked): two distinct pools of one layout (kv dtype, kv
+    heads, block size, head dim), ids in range of their own pool,
+    destinations distinct.
+    """
+    if src is dst:
+        raise ValueError("swap_blocks moves blocks between two pools; use copy_blocks within one")
+    if (src.kv_dtype, src.Hkv, src.bs, src.D) != (dst.kv_dtype, dst.Hkv, dst.bs, dst.D):
+        raise ValueError("the two pools differ in layout")
+    pairs = [(int(s), int(d)) for s, d in pairs]
+    for s, d in pairs:
+        if not 0 <= s < src.num_blocks:
+            raise IndexError(f"source block {s} outside its pool")
+        if not 0 <= d < dst.num_blocks:
+            raise IndexError(f"destination block {d} outside its pool")
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block appears twice")
+    for s, d in pairs:
+        dst.k[d] = src.k[s]
+        dst.v[d] = src.v[s]
+        if src.k_scale is not None:
+            dst.k_scale[d] = src.k_scale[s]
+            dst.v_scale[d] = src.v_scale[s]
 
 
 class OutOfBlocks(RuntimeError):

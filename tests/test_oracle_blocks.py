@@ -179,3 +179,102 @@ def test_copy_blocks_reads_the_pool_before_the_call_and_checks_pairs():
         oracle.copy_blocks(c, [(0, 4)])
     oracle.copy_blocks(c, [(3, 0), (2, 1)])
     assert [float(c.k[b].flat[0]) for b in range(4)] == [3.0, 2.0, 2.0, 3.0]
+
+
+# ---- swap between a GPU pool and a host pool --------------------------------
+
+
+def _swap_round_trip(kv_dtype, swap):
+    """Swap one sequence's blocks out to a host pool, let another sequence
+    reuse (overwrite) its GPU blocks, swap it back in under other ids and
+    rewrite its table: its decode is exactly what it was.  Returns True when
+    that holds."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, bs = 4, 2, 32, 16
+    lens = [37, 50, 16]
+    Ks = [pinlib.dyadic(rng, (L, Hkv, D)) for L in lens]
+    Vs = [pinlib.dyadic(rng, (L, Hkv, D)) for L in lens]
+    cache, tb, cl = pinlib.paged_from_dense(Ks, Vs, bs, kv_dtype, rng, spare=8)
+    q = pinlib.dyadic(rng, (len(lens), Hq, D))
+    before = oracle.decode(q, cache, tb, cl, 0.3)
+    victim = 1
+    nblk = -(-lens[victim] // bs)
+    gpu_ids = [int(b) for b in tb[victim, :nblk]]
+    host = oracle.PagedCache.empty(kv_dtype, 9, Hkv, bs, D)
+    host_ids = [8 - i for i in range(nblk)]
+    swap(cache, host, list(zip(gpu_ids, host_ids)))
+    # the freed GPU blocks are reused by someone else
+    cache.k[gpu_ids] = cache.k[0]
+    cache.v[gpu_ids] = -cache.v[0]
+    if cache.k_scale is not None:
+        cache.k_scale[gpu_ids] = 0
+        cache.v_scale[gpu_ids] = 0
+    used = {int(b) for b in tb[tb >= 0].ravel()}
+    free = [b for b in range(cache.num_blocks) if b not in used]
+    new_ids = free[:nblk]
+    swap(host, cache, list(zip(host_ids, new_ids)))
+    tb2 = tb.copy()
+    tb2[victim, :nblk] = new_ids
+    after = oracle.decode(q, cache, tb2, cl, 0.3)
+    return np.array_equal(after, before)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "i8"])
+def test_swap_out_and_in_decodes_exactly_as_before(kv_dtype):
+    """A preempted sequence's KV moved to host memory and back under new
+    block ids decodes bit for bit as before (page "vLLM框架是怎么做推理加速的",
+    section 2: swapped requests resume; page "字节跳动 AI Infra (2)",
+    PagedAttention question: KV swapped to CPU when memory runs short)."""
+    assert _swap_round_trip(kv_dtype, oracle.swap_blocks)
+
+
+def _swap_k_only(src, dst, pairs):
+    for s, d in pairs:
+        dst.k[d] = src.k[s]
+
+
+def _swap_without_scales(src, dst, pairs):
+    for s, d in pairs:
+        dst.k[d] = src.k[s]
+        dst.v[d] = src.v[s]
+
+
+def _swap_first_head_only(src, dst, pairs):
+    for s, d in pairs:
+        dst.k[d, 0] = src.k[s, 0]
+        dst.v[d, 0] = src.v[s, 0]
+        if src.k_scale is not None:
+            dst.k_scale[d] = src.k_scale[s]
+            dst.v_scale[d] = src.v_scale[s]
+
+
+@pytest.mark.parametrize("mutant,kv_dtype", [(_swap_k_only, "bf16"), (_swap_without_scales, "i8"),
+                                             (_swap_first_head_only, "f32")])
+def test_swap_mutants_are_caught(mutant, kv_dtype):
+    assert not _swap_round_trip(kv_dtype, mutant)
+
+
+def test_swap_moves_exactly_the_blocks_and_checks_its_arguments():
+    rng = np.random.default_rng(3)
+    g = oracle.PagedCache.empty("i8", 5, 2, 16, 32, poison=False)
+    K = pinlib.dyadic(rng, (5 * 16, 2, 32))
+    oracle.append(g, K, -K, np.arange(5 * 16))
+    h = oracle.PagedCache.empty("i8", 3, 2, 16, 32)
+    g_before = (g.k.copy(), g.v.copy(), g.k_scale.copy(), g.v_scale.copy())
+    h_before = (h.k.copy(), h.v.copy(), h.k_scale.copy(), h.v_scale.copy())
+    oracle.swap_blocks(g, h, [(4, 0), (1, 2)])
+    for a, b in zip((g.k, g.v, g.k_scale, g.v_scale), g_before):
+        assert np.array_equal(a, b)  # the source pool is only read
+    for got, src_arr, untouched in zip((h.k, h.v, h.k_scale, h.v_scale), g_before, h_before):
+        assert np.array_equal(got[0], src_arr[4]) and np.array_equal(got[2], src_arr[1])
+        assert np.array_equal(got[1], untouched[1], equal_nan=True)
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(g, g, [(0, 1)])  # one pool: that is copy_blocks
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(g, oracle.PagedCache.empty("i8", 3, 2, 32, 32), [(0, 0)])  # layouts differ
+    with pytest.raises(IndexError):
+        oracle.swap_blocks(g, h, [(5, 0)])
+    with pytest.raises(IndexError):
+        oracle.swap_blocks(g, h, [(0, 3)])
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(g, h, [(0, 1), (2, 1)])
