@@ -271,6 +271,46 @@ def time_multi(case: Case, steps: int, warmup: int, flush, perfmodel, q_len: int
             "GBps": round(nbytes / us / 1e3, 1), "frac_of_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)}
 
 
+def time_swap(case: Case, steps: int, warmup: int, max_pairs: int = 1024) -> dict:
+    """pa_swap_blocks: used blocks of the workload's pool out to a pinned host
+    pool and back into unused GPU blocks (the preemption copy), timed per
+    direction with HIP events."""
+    torch, pa = case.torch, case.pa
+    import numpy as np
+
+    used = case.w.used_blocks()
+    free = np.setdiff1d(np.arange(case.w.num_blocks), used)
+    n = int(min(max_pairs, len(used), len(free)))
+    if n == 0:
+        return {}
+    s = case.s
+    host = pa.KVCache.allocate(n, s.Hkv, s.bs, s.D, s.kv_dtype, device="cpu")
+    rng = np.random.default_rng(6)
+    src = rng.choice(used, n, replace=False)
+    dst = rng.choice(free, n, replace=False)
+    dev = case.q.device
+    out_pairs = torch.from_numpy(np.stack([src, np.arange(n)], 1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), dst], 1).astype(np.int32)).to(dev)
+    res = {}
+    for name, a, b, pairs in (("out", case.cache, host, out_pairs), ("in", host, case.cache, in_pairs)):
+        for _ in range(warmup):
+            pa.swap_blocks(a, b, pairs)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record()
+            pa.swap_blocks(a, b, pairs)
+            e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        elem = {"f32": 4, "bf16": 2, "i8": 1}[s.kv_dtype]
+        per_block = s.Hkv * s.bs * s.D * elem * 2 + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype == "i8" else 0)
+        res[name] = {"us": round(us, 2), "GBps": round(n * per_block / us / 1e3, 1)}
+    res.update({"pairs": n, "bytes_each_way": n * per_block})
+    del host
+    return res
+
+
 # multi-query shapes beyond the headline workload's 4-token step: (name, heads,
 # kv heads, cached tokens per sequence, new tokens per sequence, sequences)
 MULTI_SHAPES = [
@@ -488,6 +528,8 @@ def main(argv=None) -> int:
     out32 = case.decode_f32().cpu().numpy()
     copy_stats = time_copy_blocks(case, args.steps, args.warmup, flush)
     log(f"copy_blocks: {copy_stats}")
+    swap_stats = time_swap(case, min(args.steps, 10), min(args.warmup, 2))
+    log(f"swap_blocks: {swap_stats}")
     multi_stats = time_multi(case, args.steps, args.warmup, flush, perfmodel) if not case.split else {}
     log(f"decode_multi: {multi_stats}")
 
@@ -535,6 +577,7 @@ def main(argv=None) -> int:
         "bytes_per_step": head["bytes"],
         "roofline": roofline,
         "copy_blocks": copy_stats,
+        "swap_blocks": swap_stats,
         "decode_multi": multi_stats,
     }
 

@@ -242,6 +242,36 @@ pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_se
 pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs, hipStream_t stream);
 
 /*
+ * pa_swap_blocks -- copy whole physical blocks from one pool to another of
+ * the same layout: the GPU pool and a host pool, for preemption.
+ *
+ * When GPU memory runs short, or a request is preempted, its blocks are
+ * moved to CPU memory and brought back before it runs again (page
+ * "字节跳动 AI Infra (2)", PagedAttention question, scheduling list; page
+ * "vLLM框架是怎么做推理加速的", section 2 and its second follow-up).  For
+ * each i < num_pairs, block block_pairs[2i] of `src` is copied to block
+ * block_pairs[2i + 1] of `dst`: every K and V element of every kv head and,
+ * for int8 caches, every scale.  A block's contents do not depend on where
+ * it lives: after swapping out and back in under new ids (and rewriting the
+ * block table) a sequence decodes bit for bit as before.
+ *
+ *   src, dst     pools of the same kv_dtype, num_kv_heads, block_size and
+ *                head_dim (else PA_ERR_BAD_SHAPE).  Either may be host memory
+ *                that the GPU can address: allocated pinned (hipHostMalloc;
+ *                torch's pin_memory=True), not registered after the fact.
+ *                The kernel reads and writes it directly over the bus.
+ *   block_pairs  int32 [num_pairs][2] (source id in src, destination id in
+ *                dst), device memory or pinned host memory, 4-byte aligned
+ * Preconditions (device data): destinations distinct; if src and dst are the
+ * same pool, no destination is also a source.  Pairs with an id outside its
+ * pool are skipped.  The copy is ordered on `stream` like any kernel: host
+ * code reads a host destination only after synchronising with the stream.
+ * num_pairs == 0 is a no-op.
+ */
+pa_status pa_swap_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs,
+                         int32_t num_pairs, hipStream_t stream);
+
+/*
  * Block manager -- host bookkeeping of a block pool (no GPU work).
  *
  * Reference counts of num_blocks physical blocks of block_size tokens.  Blocks

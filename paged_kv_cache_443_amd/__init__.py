@@ -29,6 +29,7 @@ __all__ = [
     "split_workspace_bytes",
     "max_partitions",
     "copy_blocks",
+    "swap_blocks",
     "BlockManager",
     "OutOfBlocks",
 ]
@@ -60,9 +61,9 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, shape=None) -> None:
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, host_ok: bool = False) -> None:
+    if not (t.is_cuda or (host_ok and t.device.type == "cpu" and t.is_pinned())):
+        raise ValueError(f"{name} must be a GPU tensor" + (" or pinned host memory" if host_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -107,25 +108,29 @@ class KVCache:
     @classmethod
     def allocate(cls, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str,
                  device="cuda") -> "KVCache":
-        """Uninitialised pools (torch.empty) of the library's layout."""
+        """Uninitialised pools (torch.empty) of the library's layout.  ``device="cpu"``
+        gives pinned host pools (the host side of ``swap_blocks``)."""
         ks, vs, ss = cls.shapes(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
         dt = _KV_TORCH[kv_dtype]
-        k = torch.empty(ks, dtype=dt, device=device)
-        v = torch.empty(vs, dtype=dt, device=device)
+        pin = torch.device(device).type == "cpu"
+        k = torch.empty(ks, dtype=dt, device=device, pin_memory=pin)
+        v = torch.empty(vs, dtype=dt, device=device, pin_memory=pin)
         sk = sv = None
         if kv_dtype == "i8":
-            sk = torch.empty(ss, dtype=torch.float16, device=device)
-            sv = torch.empty(ss, dtype=torch.float16, device=device)
+            sk = torch.empty(ss, dtype=torch.float16, device=device, pin_memory=pin)
+            sv = torch.empty(ss, dtype=torch.float16, device=device, pin_memory=pin)
         return cls(k, v, sk, sv, num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
 
-    def descriptor(self) -> PaKvCache:
+    def descriptor(self, host_ok: bool = False) -> PaKvCache:
+        """The C descriptor.  Pools must be on the GPU, or pinned host memory
+        where ``host_ok`` (the swap)."""
         ks, vs, ss = self.shapes(self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim, self.kv_dtype)
         dt = _KV_TORCH[self.kv_dtype]
-        _need(self.k_cache, "k_cache", dt, ks)
-        _need(self.v_cache, "v_cache", dt, vs)
+        _need(self.k_cache, "k_cache", dt, ks, host_ok)
+        _need(self.v_cache, "v_cache", dt, vs, host_ok)
         if self.kv_dtype == "i8":
-            _need(self.k_scale, "k_scale", torch.float16, ss)
-            _need(self.v_scale, "v_scale", torch.float16, ss)
+            _need(self.k_scale, "k_scale", torch.float16, ss, host_ok)
+            _need(self.v_scale, "v_scale", torch.float16, ss, host_ok)
         return PaKvCache(_ptr(self.k_cache), _ptr(self.v_cache), _ptr(self.k_scale), _ptr(self.v_scale),
                          self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim,
                          {"f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8}[self.kv_dtype])
@@ -245,6 +250,21 @@ def copy_blocks(cache: KVCache, block_pairs: torch.Tensor) -> None:
     st = _lib.lib().pa_copy_blocks(ctypes.byref(desc), _ptr(block_pairs), block_pairs.shape[0],
                                    _stream(block_pairs.device))
     _check("pa_copy_blocks", st)
+
+
+def swap_blocks(src: KVCache, dst: KVCache, block_pairs: torch.Tensor, stream_device="cuda") -> None:
+    """Copy whole blocks from pool ``src`` to pool ``dst`` (the same layout; either
+    may be a pinned host pool from ``KVCache.allocate(..., device="cpu")``).
+    ``block_pairs`` int32 ``[n, 2]`` (id in src, id in dst), on the GPU or
+    pinned.  Runs on the current stream of ``stream_device``; synchronise
+    before reading a host destination."""
+    _need(block_pairs, "block_pairs", torch.int32, host_ok=True)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    ds, dd = src.descriptor(host_ok=True), dst.descriptor(host_ok=True)
+    st = _lib.lib().pa_swap_blocks(ctypes.byref(ds), ctypes.byref(dd), _ptr(block_pairs), block_pairs.shape[0],
+                                   _stream(torch.device(stream_device)))
+    _check("pa_swap_blocks", st)
 
 
 class OutOfBlocks(PAError):

@@ -30,6 +30,7 @@ EXPORTED = (
     "pa_decode_split",
     "pa_reduce",
     "pa_copy_blocks",
+    "pa_swap_blocks",
     "pa_bm_create",
     "pa_bm_destroy",
     "pa_bm_num_free",
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.pa_reduce.restype = c_int
     L.pa_copy_blocks.argtypes = [P, c_void_p, c_int32, c_void_p]
     L.pa_copy_blocks.restype = c_int
+    L.pa_swap_blocks.argtypes = [P, P, c_void_p, c_int32, c_void_p]
+    L.pa_swap_blocks.restype = c_int
     I32P = ctypes.POINTER(c_int32)
     L.pa_bm_create.argtypes = [c_int32, c_int32, ctypes.POINTER(c_void_p)]
     L.pa_bm_create.restype = c_int

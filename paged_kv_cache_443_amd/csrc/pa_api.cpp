@@ -73,6 +73,29 @@ pa_status launch(pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stre
   return from_hip(e);
 }
 
+pa_status launch_block_copies(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs,
+                              int32_t num_pairs, hipStream_t stream) {
+  if (static_cast<int64_t>(num_pairs) * src->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  static const int32_t kElem[] = {4, 2, 1};  // PA_F32, PA_BF16, PA_I8
+  pa::CopyParams p{};
+  p.src_k = src->k_cache;
+  p.src_v = src->v_cache;
+  p.src_k_scale = src->k_scale;
+  p.src_v_scale = src->v_scale;
+  p.dst_k = dst->k_cache;
+  p.dst_v = dst->v_cache;
+  p.dst_k_scale = dst->k_scale;
+  p.dst_v_scale = dst->v_scale;
+  p.pairs = block_pairs;
+  p.num_pairs = num_pairs;
+  p.num_kv_heads = src->num_kv_heads;
+  p.src_blocks = src->num_blocks;
+  p.dst_blocks = dst->num_blocks;
+  p.block_size = src->block_size;
+  p.tile_bytes = static_cast<size_t>(src->block_size) * src->head_dim * kElem[src->kv_dtype];
+  return from_hip(pa::launch_copy_blocks(p, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,20 +210,14 @@ pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, i
                          hipStream_t stream) {
   pa_status st = pa::check_copy(cache, block_pairs, num_pairs);
   if (st != PA_OK || num_pairs == 0) return st;
-  if (static_cast<int64_t>(num_pairs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
-  static const int32_t kElem[] = {4, 2, 1};  // PA_F32, PA_BF16, PA_I8
-  pa::CopyParams p{};
-  p.k_cache = cache->k_cache;
-  p.v_cache = cache->v_cache;
-  p.k_scale = cache->k_scale;
-  p.v_scale = cache->v_scale;
-  p.pairs = block_pairs;
-  p.num_pairs = num_pairs;
-  p.num_kv_heads = cache->num_kv_heads;
-  p.num_blocks = cache->num_blocks;
-  p.block_size = cache->block_size;
-  p.tile_bytes = static_cast<size_t>(cache->block_size) * cache->head_dim * kElem[cache->kv_dtype];
-  return from_hip(pa::launch_copy_blocks(p, stream));
+  return launch_block_copies(cache, cache, block_pairs, num_pairs, stream);
+}
+
+pa_status pa_swap_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs,
+                         int32_t num_pairs, hipStream_t stream) {
+  pa_status st = pa::check_swap(src, dst, block_pairs, num_pairs);
+  if (st != PA_OK || num_pairs == 0) return st;
+  return launch_block_copies(src, dst, block_pairs, num_pairs, stream);
 }
 
 size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {

@@ -71,15 +71,22 @@ struct AppendParams {
   int32_t num_blocks;
 };
 
+// Whole-block copies from one pool to another of the same layout (the same
+// pool for copy-on-write; a GPU pool and a pinned host pool for a swap).
 struct CopyParams {
-  void *k_cache;
-  void *v_cache;
-  void *k_scale;              // int8 caches only, else null
-  void *v_scale;
-  const int32_t *pairs;       // [num_pairs][2] (source, destination)
+  const void *src_k;
+  const void *src_v;
+  const void *src_k_scale;    // int8 caches only, else null
+  const void *src_v_scale;
+  void *dst_k;
+  void *dst_v;
+  void *dst_k_scale;
+  void *dst_v_scale;
+  const int32_t *pairs;       // [num_pairs][2] (source block, destination block)
   int32_t num_pairs;
   int32_t num_kv_heads;
-  int32_t num_blocks;
+  int32_t src_blocks;         // blocks in the source pool
+  int32_t dst_blocks;         // blocks in the destination pool
   int32_t block_size;
   size_t tile_bytes;          // one (block, kv head) tile of one pool
 };

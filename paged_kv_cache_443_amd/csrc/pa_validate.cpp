@@ -124,6 +124,21 @@ pa_status check_copy(const pa_kv_cache *cache, const int32_t *block_pairs, int32
   return PA_OK;
 }
 
+pa_status check_swap(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs, int32_t num_pairs) {
+  pa_status st = check_cache(src);
+  if (st != PA_OK) return st;
+  st = check_cache(dst);
+  if (st != PA_OK) return st;
+  if (src->kv_dtype != dst->kv_dtype || src->num_kv_heads != dst->num_kv_heads ||
+      src->block_size != dst->block_size || src->head_dim != dst->head_dim)
+    return PA_ERR_BAD_SHAPE;
+  if (num_pairs < 0) return PA_ERR_BAD_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (block_pairs == nullptr) return PA_ERR_NULL_PTR;
+  if (!aligned(block_pairs, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
 size_t split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
   if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_num_partitions < 1) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * max_num_partitions;

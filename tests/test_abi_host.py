@@ -116,6 +116,25 @@ def test_multi_rejections(L):
                              None) == PA_OK
 
 
+def test_swap_rejections(L):
+    g, h = _cache(nb=8), _cache(nb=3, k=A16[11], v=A16[12])
+
+    def swap(src=g, dst=h, pairs=A16[13], n=2):
+        return L.pa_swap_blocks(ctypes.byref(src), ctypes.byref(dst), pairs, n, None)
+
+    assert swap(pairs=None) == PA_ERR_NULL_PTR
+    assert swap(pairs=A16[13] + 2) == PA_ERR_MISALIGNED
+    assert swap(n=-1) == PA_ERR_BAD_SHAPE
+    assert swap(dst=_cache(nb=3, k=A16[11], v=A16[12], bs=32)) == PA_ERR_BAD_SHAPE  # layouts differ
+    assert swap(dst=_cache(nb=3, k=A16[11], v=A16[12], D=64)) == PA_ERR_BAD_SHAPE
+    assert swap(dst=_cache(nb=3, k=A16[11], v=A16[12], H=4)) == PA_ERR_BAD_SHAPE
+    assert swap(dst=_cache(kv=PA_I8, nb=3, k=A16[11], v=A16[12])) == PA_ERR_BAD_SHAPE
+    assert swap(dst=_cache(nb=3, k=None)) == PA_ERR_NULL_PTR
+    assert swap(src=_cache(k=A16[0] + 8)) == PA_ERR_MISALIGNED
+    assert L.pa_swap_blocks(None, ctypes.byref(h), A16[13], 2, None) == PA_ERR_NULL_PTR
+    assert swap(pairs=None, n=0) == PA_OK  # no pairs: a no-op
+
+
 def _split(L, cache, P=512, Pmax=1, po=A16[8], pl=A16[9], mbps=8, B=4):
     return L.pa_decode_split(A16[4], PA_BF16, B, 8, ctypes.byref(cache), A16[5], mbps, A16[6], 0.1, P, Pmax, po, pl,
                              None)
