@@ -364,6 +364,50 @@ def time_multi_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush
             "frac_of_mfma_peak": round(flops / us / 1e6 / perfmodel.MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+# single-token decode with a whole MQA group on one kv head: (name, heads,
+# kv heads, cached tokens per sequence, sequences, kv dtype)
+MQA_SHAPES = [
+    ("mqa64-bf16", 64, 1, 4096, 128, "bf16"),
+    ("mqa64-int8", 64, 1, 4096, 128, "i8"),
+]
+
+
+def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush) -> dict:
+    """pa_decode on a synthetic cache of its own (D 128, bs 16)."""
+    from workloads import make_custom
+    from workloads.device import append_tokens, meta
+
+    name, Hq, Hkv, L, B, kv = shape
+    w = make_custom(B=B, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype=kv, lengths=[L] * B, seed=12)
+    dev = torch.device("cuda:0")
+    cache = pa.KVCache.allocate(w.num_blocks, Hkv, 16, 128, kv, dev)
+    append_tokens(w, cache)
+    q, tables, lens = meta(w)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        pa.decode(q, cache, tables, lens, w.spec.scale, out)
+
+    for _ in range(warmup):
+        flush()
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = perfmodel.decode_bytes(w.context_lens, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype=kv, q_dtype="bf16",
+                                    out_dtype="bf16")
+    del cache, out
+    torch.cuda.empty_cache()
+    return {"batch": B, "cached_tokens": L, "q_heads": Hq, "kv_heads": Hkv, "kv_dtype": kv, "us": round(us, 2),
+            "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)}
+
+
 def summarise(case: Case, t: dict, peak: float) -> dict:
     s = case.s
     step_us = t["step"]["mean_us"]
@@ -593,6 +637,11 @@ def main(argv=None) -> int:
             shapes[shape[0]] = time_multi_shape(torch, pa, perfmodel, shape, args.steps, args.warmup, flush)
             log(f"decode_multi {shape[0]}: {shapes[shape[0]]}")
         multi_stats["shapes"] = shapes
+        mqa = {}
+        for shape in MQA_SHAPES:
+            mqa[shape[0]] = time_decode_shape(torch, pa, perfmodel, shape, args.steps, args.warmup, flush)
+            log(f"decode {shape[0]}: {mqa[shape[0]]}")
+        line["decode_mqa"] = mqa
 
     other = {}
     for c in others:

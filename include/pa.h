@@ -159,10 +159,9 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
  * to and including its own:
  *     out[r][h] = sum_{t <= L - n_b + i} softmax_t(scale * q[r][h] . k_t) v_t
  * (the step-t attention of page "字节跳动 AI Infra (2)", KV-cache question,
- * taken for each new token in turn).  With max_q_len == 1 and at most 16
- * query heads per kv head this is pa_decode, bit for bit; otherwise the
- * fp32 summation order may differ (the launch shape depends on
- * max_q_len * num_heads / num_kv_heads).
+ * taken for each new token in turn).  With max_q_len == 1 this is
+ * pa_decode, bit for bit; a larger bound may change the fp32 summation
+ * order (the launch shape depends on max_q_len * num_heads / num_kv_heads).
  *
  *   q             [num_queries][num_heads][head_dim], BF16, 16-byte aligned
  *   q_start       int32 [num_seqs + 1], non-decreasing, q_start[0] == 0,

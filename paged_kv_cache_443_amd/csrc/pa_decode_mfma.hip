@@ -364,7 +364,7 @@ __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<
 // A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
 // while the previous one is computed.
 template <bool I8, int D, int BS, int NW, bool CAUSAL = false, bool NT = true>
-__device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
+__device__ __forceinline__ void stream_chunks(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
                                                 int c0, int n, float scale_log2) {
   constexpr int STEP = NW * Tile<I8, D>::CT;
   KBuf<I8, D> kb;
@@ -385,44 +385,6 @@ __device__ __forceinline__ void stream_chunks_1(State<I8, D> &st, const Ctx<I8, 
   consume<I8, D, BS, true, false, CAUSAL, NT>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
 }
 
-// The same with two chunks in flight: buffers A and B alternate; chunk i is in
-// A for even i and in B for odd i.
-template <bool I8, int D, int BS, int NW>
-__device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
-                                                int c0, int n, float scale_log2) {
-  constexpr int STEP = NW * Tile<I8, D>::CT;
-  KBuf<I8, D> ka, kb;
-  VBuf<I8, D> va, vb;
-  {
-    const Ids i0 = read_ids(x, c0);
-    issue_k<true>(ka, x, c0, i0);
-    issue_v<true>(va, x, c0, i0);
-    if (n > 1) {
-      const Ids i1 = read_ids(x, c0 + STEP);
-      issue_k<true>(kb, x, c0 + STEP, i1);
-      issue_v<true>(vb, x, c0 + STEP, i1);
-    }
-  }
-  int i = 0;
-  for (; i + 2 < n; i += 2) {
-    const int ci = c0 + i * STEP;
-    consume<I8, D, BS, false, true>(st, ka, va, x, qop, ci, ci + 2 * STEP, read_ids(x, ci + 2 * STEP), scale_log2);
-    if (i + 3 < n)
-      consume<I8, D, BS, false, true>(st, kb, vb, x, qop, ci + STEP, ci + 3 * STEP, read_ids(x, ci + 3 * STEP),
-                                      scale_log2);
-    else
-      consume<I8, D, BS, false, false>(st, kb, vb, x, qop, ci + STEP, 0, Ids{0, 0}, scale_log2);
-  }
-  // chunk i is in A; chunk i + 1, if any, is in B and is the last one
-  const int ci = c0 + i * STEP;
-  if (i + 1 < n) {
-    consume<I8, D, BS, false, false>(st, ka, va, x, qop, ci, 0, Ids{0, 0}, scale_log2);
-    consume<I8, D, BS, true, false>(st, kb, vb, x, qop, ci + STEP, 0, Ids{0, 0}, scale_log2);
-  } else {
-    consume<I8, D, BS, true, false>(st, ka, va, x, qop, ci, 0, Ids{0, 0}, scale_log2);
-  }
-}
-
 // One unit of work: (sequence b, kv head x query-head group hx[, partition]).
 // Every thread of the work-group calls it with the same arguments.  On entry
 // the LDS table window and merge buffers may be reused (the previous unit's
@@ -437,11 +399,9 @@ __device__ __forceinline__ void stream_chunks_2(State<I8, D> &st, const Ctx<I8, 
 // group w % R and takes every (NW / R)-th chunk of that group's tokens, so
 // the R groups walk the same K/V chunks at about the same time and all but
 // the first read of each line come from the cache.
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
+template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<I8, D>;
-  static_assert(!CAUSAL || DEPTH == 1, "causal rows use the one-deep stream");
-  static_assert(R == 1 || CAUSAL, "several row groups per unit only for multi-query units");
   static_assert(NW % R == 0, "row groups must divide the wavefronts");
   constexpr int NWT = NW / R;  // wavefronts sharing one row group's tokens
   const int lane = threadIdx.x & 63;
@@ -501,6 +461,8 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int r_last = min(nrows, (rg0 + R) * 16) - 1;
     t1u = min(x.t1, L - nq + r_last / p.group + 1);
     x.t1 = gcount > 0 ? min(x.t1, L - nq + (r0 + gcount - 1) / p.group + 1) : t0;
+  } else if constexpr (R > 1) {
+    if (gcount <= 0) x.t1 = t0;  // a row slot past the last query head
   }
   x.nbv = (x.t1 + BS - 1) / BS;
 
@@ -550,12 +512,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int wew = R == 1 ? we : min(we, x.t1);
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
-    if (n > 0) {
-      if constexpr (DEPTH == 1)
-        stream_chunks_1<I8, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
-      else
-        stream_chunks_2<I8, D, BS, NWT>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
-    }
+    if (n > 0) stream_chunks<I8, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
@@ -621,7 +578,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
+template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -664,7 +621,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<I8, D, BS, NW, DEPTH, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<I8, D, BS, NW, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -675,7 +632,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // a piece index then maps to its sequence by binary search.  No work-group is
 // spent on a partition past the end of its sequence, and the pieces are of
 // near-equal size, so a static stride balances the work.
-template <bool I8, int D, int BS, int NW, int DEPTH>
+template <bool I8, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -728,18 +685,18 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
     }
     const int local = piece - sm.first[lo];
     const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
-    if (n_b > 0) run_unit<I8, D, BS, NW, DEPTH>(p, sm, lo, local / n_b, local % n_b);
+    if (n_b > 0) run_unit<I8, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
   }
 }
 
 // Split pass: persistent when the sequences' piece offsets fit in LDS,
 // else one work-group per (unit, partition).
-template <bool I8, int D, int BS, int NW, int DEPTH>
+template <bool I8, int D, int BS, int NW>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   const int rows = p.rows_per_group;
   if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
-    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW, DEPTH>;
+    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW>;
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -753,7 +710,7 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   }
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_num_partitions;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
                      lds, s, p);
   return hipGetLastError();
 }
@@ -763,27 +720,42 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
 // than one work-group, so that another one streams while a work-group ranks
 // (measured: +3 points for four-wave int8 units; with one eight-wave
 // work-group per CU the ranking is dead time and cost 2 points).
-template <bool I8, int D, int BS, int NW, int DEPTH, bool CAUSAL = false, int R = 1>
+template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
   p.lpt = (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
   p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, DEPTH, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
                      dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
 
-// Causal multi-query: R = row groups per unit, the smallest power of two that
-// covers a sequence's row groups, at most the wavefront count.
-template <bool I8, int D, int BS, int NW>
-hipError_t launch_causal(const DecodeParams &p, hipStream_t s) {
+// R = row groups per unit.  More than one row group per (sequence, kv head):
+// a multi-query unit, or a single-token unit with more than 16 query heads per
+// kv head (MQA-like groups).  Packing the groups of a kv head into one unit
+// reads its K/V from HBM once instead of once per group, but splits each
+// group's tokens between fewer wavefronts, each holding one chunk in flight.
+// Units with several query tokens are compute-heavy: all groups in one unit
+// (R up to the wavefront count; 512-token chunks ran 2.5x faster than one
+// group per unit).  Single-token units stream: two groups per unit (on one kv
+// head with 32 to 128 query heads, bf16 and int8, two per unit beat one by
+// 1.1-2.0x and four or eight by 1.3-2.4x).  The choice depends on the launch
+// shape only, so a multi-query launch with one token per sequence is the
+// single-token launch.
+template <bool I8, int D, int BS, int NW, bool CAUSAL>
+hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
   const int rg = p.head_groups;  // row groups of a (sequence, kv head)
-  if (rg <= 1) return launch_single<I8, D, BS, NW, 1, true, 1>(p, s);
-  if (rg <= 2) return launch_single<I8, D, BS, NW, 1, true, 2>(p, s);
-  if (rg <= 4 || NW == 4) return launch_single<I8, D, BS, NW, 1, true, 4>(p, s);
-  return launch_single<I8, D, BS, NW, 1, true, (NW >= 8 ? 8 : 4)>(p, s);
+  const int most = p.max_q_len > 1 ? NW : 2;
+  int r = 1;
+  while (r < rg && r < most) r *= 2;
+  switch (r) {
+    case 1: return launch_single<I8, D, BS, NW, CAUSAL, 1>(p, s);
+    case 2: return launch_single<I8, D, BS, NW, CAUSAL, 2>(p, s);
+    case 4: return launch_single<I8, D, BS, NW, CAUSAL, 4>(p, s);
+  }
+  return launch_single<I8, D, BS, NW, CAUSAL, (NW >= 8 ? 8 : 4)>(p, s);
 }
 
 // Wavefronts per unit.  A single-pass bf16 unit is a whole sequence: eight
@@ -796,13 +768,13 @@ template <bool I8, int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
   const bool causal = p.q_start != nullptr;
   if constexpr (I8) {
-    if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
-    if (causal) return launch_causal<I8, D, BS, 4>(p, s);
-    return launch_single<I8, D, BS, 4, 1>(p, s);
+    if (p.partition_size > 0) return launch_split<I8, D, BS, 4>(p, s);
+    if (causal) return launch_rows<I8, D, BS, 4, true>(p, s);
+    return launch_rows<I8, D, BS, 4, false>(p, s);
   } else {
-    if (p.partition_size > 0) return launch_split<I8, D, BS, 4, 1>(p, s);
-    if (causal) return launch_causal<I8, D, BS, 8>(p, s);
-    return launch_single<I8, D, BS, 8, 1>(p, s);
+    if (p.partition_size > 0) return launch_split<I8, D, BS, 4>(p, s);
+    if (causal) return launch_rows<I8, D, BS, 8, true>(p, s);
+    return launch_rows<I8, D, BS, 8, false>(p, s);
   }
 }
 

@@ -69,11 +69,14 @@ def test_multi_matches_oracle(case):
     assert max_err(out2, want) <= TOL[kv]
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 5, "mqa"])
 def test_one_new_token_is_decode_bitwise(cfg):
-    """With one new token per sequence (max_q_len 1, at most 16 query heads
-    per kv head) the multi-query path is pa_decode, bit for bit."""
-    w = make_workload(cfg, small=True)
+    """With one new token per sequence (max_q_len 1) the multi-query path is
+    pa_decode, bit for bit."""
+    if cfg == "mqa":  # 40 query heads on one kv head: three row groups per unit
+        w = make_custom(B=5, Hq=40, Hkv=1, D=128, bs=16, kv_dtype="bf16", lengths=[1, 77, 300, 16, 513], seed=5)
+    else:
+        w = make_workload(cfg, small=True)
     say(f"[multi=decode] cfg{cfg} small B={w.B}")
     oc = oracle.build_cache(w)
     cache = upload_oracle_cache(oc)

@@ -140,7 +140,7 @@ for kv in ("bf16", "i8", "f32"):
 def test_edge_lengths_and_groups(kv, bs, D):
     """Lengths around block and chunk boundaries, empty sequences, several GQA groups."""
     lens = [0, 1, bs - 1, bs, bs + 1, 31, 32, 33, 63, 64, 65, 129, 200]
-    for Hq, Hkv in ((8, 8), (8, 2), (16, 1), (32, 1), (12, 4)):
+    for Hq, Hkv in ((8, 8), (8, 2), (16, 1), (32, 1), (12, 4), (40, 1), (80, 1)):
         w = make_custom(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv, lengths=lens, seed=bs * D + Hq)
         say(f"[edge] kv={kv} bs={bs} D={D} Hq={Hq} Hkv={Hkv}")
         oc = oracle.build_cache(w)
