@@ -25,10 +25,10 @@ another precision):
   page "字节跳动 AI Infra (2)", third question, layer-2 table) -- one
   normalised partial output and log-sum-exp per token range, merged by
   weighting each range with exp(lse - max lse).
-* ``quantize_int8`` / ``append``: writing a new token's K/V into its slot,
-  as a plain copy or as symmetric int8 with one fp16 scale per
-  (token, kv head) (INT8 KV cache: page "字节跳动 AI Infra (2)", optimisation
-  table; page "LLM推理优化", section 1.3).
+* ``quantize_int8`` / ``quantize_int4`` / ``append``: writing a new token's
+  K/V into its slot, as a plain copy or as symmetric int8 (int4) with one
+  fp16 scale per (token, kv head) (INT8 KV cache: page "字节跳动 AI Infra
+  (2)", optimisation table; INT8/INT4: page "LLM推理优化", section 1.3).
 
 * ``copy_blocks`` / ``BlockManager``: copying physical blocks, and the
   reference counts, on-demand allocation, fork and copy-on-write of a block
@@ -45,7 +45,7 @@ its own code path (closed forms, invariants, pure-Python brute force, the
 pages' worked block counts); see ``tests/test_oracle_pins.py``.
 """
 from .layout import PagedCache, k_slot, x_per_16b  # noqa: F401
-from .quant import quantize_int8, dequantize_int8  # noqa: F401
+from .quant import quantize_int4, quantize_int8, dequantize_int8  # noqa: F401
 from .paged import (  # noqa: F401
     blocks_for,
     kv_head_for,

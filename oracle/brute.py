@@ -21,15 +21,21 @@ def decode_bruteforce(q, k_flat, v_flat, k_scale_flat, v_scale_flat, kv_dtype: s
 
     ``q`` is a nested list ``[B][Hq][D]`` of floats; ``k_flat``/``v_flat`` are
     the pools flattened in storage order (ints for bf16 bit patterns and
-    int8 codes, floats for fp32); scales likewise (floats) or None.
+    int8 codes, floats for fp32; for int4 the stored bytes, two codes each);
+    scales likewise (floats) or None.
     """
-    x = {"f32": 4, "bf16": 2, "i8": 1}[kv_dtype]
-    x = 16 // x
+    x = 16 if kv_dtype == "i4" else 16 // {"f32": 4, "bf16": 2, "i8": 1}[kv_dtype]
+    quantised = kv_dtype in ("i8", "i4")
     B = len(q)
     Hq = len(q[0])
     G = Hq // Hkv
 
     def load(flat, idx):
+        if kv_dtype == "i4":
+            # element idx of the unpacked order is nibble idx % 2 (low first)
+            # of byte idx // 2; a 4-bit two's-complement code
+            nib = (int(flat[idx // 2]) >> (4 * (idx % 2))) & 0xF
+            return float(nib - 16 if nib >= 8 else nib)
         raw = flat[idx]
         if kv_dtype == "bf16":
             return _bf16_to_float(raw)
@@ -44,7 +50,7 @@ def decode_bruteforce(q, k_flat, v_flat, k_scale_flat, v_scale_flat, kv_dtype: s
             slot = t - 4 * b2 - 8 * b3 + 8 * b2 + 4 * b3
         idx = (((pb * Hkv + h) * (D // x) + d // x) * bs + slot) * x + d % x
         val = load(k_flat, idx)
-        if kv_dtype == "i8":
+        if quantised:
             val *= float(k_scale_flat[(pb * Hkv + h) * bs + t])
         return val
 
@@ -52,7 +58,7 @@ def decode_bruteforce(q, k_flat, v_flat, k_scale_flat, v_scale_flat, kv_dtype: s
         # V pool [nb][Hkv][bs/x][D][x]
         idx = (((pb * Hkv + h) * (bs // x) + t // x) * D + d) * x + t % x
         val = load(v_flat, idx)
-        if kv_dtype == "i8":
+        if quantised:
             val *= float(v_scale_flat[(pb * Hkv + h) * bs + t])
         return val
 

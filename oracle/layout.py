@@ -14,6 +14,12 @@ sequences; a sequence reaches its blocks through its block table):
 * V pool ``[num_blocks][Hkv][bs/x][D][x]``: V of (pb, h, t, d) is
   ``V[pb, h, t // x, d, t % x]``;
 * int8 only: fp16 scales ``[num_blocks][Hkv][bs]`` for K and for V.
+* int4: the int8 layout with x = 16 codes per 8-byte vector: two 4-bit
+  two's-complement codes per byte, the even element of a pair in the low
+  nibble.  A K vector holds 16 channels of one token, a V vector 16 tokens
+  of one channel; the fp16 scales are those of int8.  Here the codes are
+  held unpacked (one int8 per code, same indexing as int8 with x = 16);
+  ``packed_k`` / ``packed_v`` give the stored bytes.
 
 Each (block, kv head) therefore owns ``bs * D`` contiguous elements of each
 pool, and block ``pb`` of a single-head cache starts at element
@@ -32,10 +38,18 @@ import numpy as np
 
 _ELEM_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
 _BF16_NAN = np.uint16(0x7FC0)
+QUANTISED = ("i8", "i4")
 
 
 def x_per_16b(kv_dtype: str) -> int:
-    return 16 // _ELEM_BYTES[kv_dtype]
+    """Elements per storage vector (16 bytes; int4: 8 bytes of 16 codes)."""
+    return 16 if kv_dtype == "i4" else 16 // _ELEM_BYTES[kv_dtype]
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """int4 codes ``[..., 2n]`` in [-8, 7] -> bytes ``[..., n]``, even element in the low nibble."""
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
 def k_slot(offs, kv_dtype: str):
@@ -97,8 +111,9 @@ class PagedCache:
         if kv_dtype == "bf16":
             fill = _BF16_NAN if poison else np.uint16(0)
             return cls(kv_dtype, num_blocks, Hkv, bs, D, np.full(ks, fill, np.uint16), np.full(vs, fill, np.uint16))
-        if kv_dtype == "i8":
-            fill = np.int8(-128) if poison else np.int8(0)
+        if kv_dtype in QUANTISED:
+            # poison codes are outside what the quantiser writes (-128 / -8)
+            fill = np.int8(-128 if kv_dtype == "i8" else -8) if poison else np.int8(0)
             sfill = np.float16(np.nan) if poison else np.float16(0)
             return cls(kv_dtype, num_blocks, Hkv, bs, D, np.full(ks, fill, np.int8), np.full(vs, fill, np.int8),
                        np.full((num_blocks, Hkv, bs), sfill, np.float16), np.full((num_blocks, Hkv, bs), sfill, np.float16))
@@ -138,6 +153,17 @@ class PagedCache:
         self.k[P, hh, :, k_slot(O, self.kv_dtype), :] = kraw.reshape(n, H, self.D // x, x)
         # V[pb, h, t//x, d, t%x]
         self.v[P, hh, O // x, :, O % x] = vraw
-        if self.kv_dtype == "i8":
+        if self.kv_dtype in QUANTISED:
             self.k_scale[P, hh, O] = kscale
             self.v_scale[P, hh, O] = vscale
+
+    # ---- int4 storage bytes ---------------------------------------------
+    def packed_k(self) -> np.ndarray:
+        """int4 K pool as stored: ``[num_blocks][Hkv][D/16][bs][8]`` bytes."""
+        assert self.kv_dtype == "i4"
+        return pack_nibbles(self.k)
+
+    def packed_v(self) -> np.ndarray:
+        """int4 V pool as stored: ``[num_blocks][Hkv][bs/16][D][8]`` bytes."""
+        assert self.kv_dtype == "i4"
+        return pack_nibbles(self.v)

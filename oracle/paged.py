@@ -10,7 +10,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 from .layout import PagedCache, f32_to_bf16_bits_exact
-from .quant import quantize_int8
+from .quant import quantize_int4, quantize_int8
 
 
 def blocks_for(length: int, block_size: int) -> int:
@@ -189,8 +189,9 @@ def append(cache: PagedCache, key: np.ndarray, value: np.ndarray, slot_mapping: 
     """Write tokens' K/V rows (``[T, Hkv, D]`` values) into their cache slots.
 
     Slot s >= 0 names physical block s // bs, offset s % bs; s < 0 is skipped.
-    fp32 / bf16 caches store the source values unchanged; an int8 cache
-    stores ``quantize_int8`` codes and fp16 scales per (token, kv head).
+    fp32 / bf16 caches store the source values unchanged; an int8 (int4)
+    cache stores ``quantize_int8`` (``quantize_int4``) codes and fp16 scales
+    per (token, kv head).
     Appending the new token's K and V to the cache is the concatenation step
     of the step-t equations (page "字节跳动 AI Infra (2)", KV-cache question).
     """
@@ -212,10 +213,11 @@ def append(cache: PagedCache, key: np.ndarray, value: np.ndarray, slot_mapping: 
     elif cache.kv_dtype == "bf16":
         cache.store(pbs, offs, f32_to_bf16_bits_exact(key), f32_to_bf16_bits_exact(value))
     else:
-        # the int8 cache's source tensors are bf16
+        # the quantised caches' source tensors are bf16
         f32_to_bf16_bits_exact(key), f32_to_bf16_bits_exact(value)
-        kq, ks = quantize_int8(key)
-        vq, vs = quantize_int8(value)
+        quantize = quantize_int8 if cache.kv_dtype == "i8" else quantize_int4
+        kq, ks = quantize(key)
+        vq, vs = quantize(value)
         cache.store(pbs, offs, kq, vq, ks, vs)
 
 

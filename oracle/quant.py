@@ -1,4 +1,4 @@
-"""Symmetric int8 quantisation of one (token, kv head) row, fp16 scale.
+"""Symmetric int8 and int4 quantisation of one (token, kv head) row, fp16 scale.
 
 TEST INFRASTRUCTURE (see ``oracle/__init__``).
 
@@ -36,6 +36,25 @@ def quantize_int8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     safe = np.where(nz, sf, np.float32(1.0))
     qf = np.rint((xf / safe[..., None]).astype(np.float32))  # float32 quotient, ties-to-even
     qf = np.clip(qf, -127, 127)
+    qf = np.where(nz[..., None], qf, 0)
+    return qf.astype(np.int8), s16
+
+
+def quantize_int4(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """INT4 rows (page "LLM推理优化", section 1.3, names INT4 next to INT8 for
+    the KV cache and fixes nothing else).  The same reading as int8 with the
+    symmetric 4-bit range: ``s32`` = a / 7, ``s16`` = fp16(s32), codes
+    round-half-to-even(float32(x / s16)) clamped to [-7, 7], all 0 when s16 is
+    0.  Returns (codes int8 in [-7, 7], scales fp16)."""
+    xf = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(xf), axis=-1)
+    s32 = (a / np.float32(7.0)).astype(np.float32)
+    s16 = s32.astype(np.float16)
+    sf = s16.astype(np.float32)
+    nz = sf != 0
+    safe = np.where(nz, sf, np.float32(1.0))
+    qf = np.rint((xf / safe[..., None]).astype(np.float32))
+    qf = np.clip(qf, -7, 7)
     qf = np.where(nz[..., None], qf, 0)
     return qf.astype(np.int8), s16
 

@@ -312,24 +312,24 @@ def check_split(partials, merge, decode: DecodeFn) -> None:
 # --------------------------------------------------------------------------
 
 
-def check_quant_golden(quantize) -> None:
-    for case in golden("int8_worked.json")["cases"]:
+def check_quant_golden(quantize, name: str = "int8_worked.json") -> None:
+    for case in golden(name)["cases"]:
         x = np.array(case["x"], np.float32)[None, :]
         codes, scale = quantize(x)
         assert float(scale[0]) == case["scale"], (case, float(scale[0]))
         assert codes[0].tolist() == case["codes"], (case, codes[0].tolist())
 
 
-def check_quant_invariants(quantize) -> None:
+def check_quant_invariants(quantize, qmax: int = 127) -> None:
     rng = np.random.default_rng(19)
     from workloads import bf16_round
     x = bf16_round((rng.standard_normal((4000, 64)) * rng.uniform(1e-3, 50, (4000, 1))).astype(np.float32))
     codes, s16 = quantize(x)
     s = s16.astype(np.float64)
-    # the largest-magnitude element maps to +-127
+    # the largest-magnitude element maps to +-qmax
     i = np.argmax(np.abs(x), axis=1)
     top = codes[np.arange(len(x)), i].astype(np.int64)
-    assert np.all(np.abs(top) == 127)
+    assert np.all(np.abs(top) == qmax)
     assert np.all(np.sign(top) == np.sign(x[np.arange(len(x)), i]))
     # reconstruction error at most half a step
     err = np.abs(codes.astype(np.float64) * s[:, None] - x.astype(np.float64))
@@ -337,17 +337,17 @@ def check_quant_invariants(quantize) -> None:
     # the scale is the fp16 nearest to absmax/127 (checked with exact rationals)
     from fractions import Fraction
     for r in range(0, 4000, 397):
-        a = Fraction(float(np.max(np.abs(x[r])))) / 127
+        a = Fraction(float(np.max(np.abs(x[r])))) / qmax
         got = Fraction(float(s16[r]))
         # neighbours of got in fp16
         up = Fraction(float(np.nextafter(s16[r], np.float16(np.inf))))
         dn = Fraction(float(np.nextafter(s16[r], np.float16(0))))
         assert abs(got - a) <= abs(up - a) and abs(got - a) <= abs(dn - a)
-    # codes never use -128
-    assert codes.min() >= -127
+    # codes never use the most negative value of the type (-128 / -8)
+    assert codes.min() >= -qmax and codes.max() <= qmax
 
 
-def check_quant_rounding_exact(quantize, n: int = 20000) -> None:
+def check_quant_rounding_exact(quantize, n: int = 20000, qmax: int = 127) -> None:
     """The float32 quotient rounds to the same integer as the exact quotient
     (so taking the decision in float32 equals the exact rule)."""
     from fractions import Fraction
@@ -365,5 +365,5 @@ def check_quant_rounding_exact(quantize, n: int = 20000) -> None:
             fl = qx.numerator // qx.denominator
             rem = qx - fl
             want = fl + 1 if rem > Fraction(1, 2) else fl if rem < Fraction(1, 2) else (fl if fl % 2 == 0 else fl + 1)
-            want = max(-127, min(127, want))
+            want = max(-qmax, min(qmax, want))
             assert int(codes[r, d]) == want, (r, d, float(x[r, d]), float(s16[r]))
