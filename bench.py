@@ -74,14 +74,14 @@ def parse_args(argv=None):
 class Case:
     """A workload resident on the GPU, with its step and its byte counts."""
 
-    def __init__(self, cfg: int, seed, torch, pa, perfmodel):
+    def __init__(self, cfg: int, seed, torch, pa, perfmodel, **overrides):
         from workloads import make_workload
         from workloads.device import append_tokens, meta, new_token_batch, poisoned_cache
 
         self.torch = torch
         self.pa = pa
         t0 = time.time()
-        self.w = w = make_workload(cfg, seed)
+        self.w = w = make_workload(cfg, seed, **overrides)
         s = self.s = w.spec
         log(f"cfg{cfg} {s.name}: B={w.B} tokens={w.total_tokens()} pool={w.num_blocks} blocks; filling cache")
         self.cache = poisoned_cache(w)
@@ -650,6 +650,16 @@ def main(argv=None) -> int:
         ot = time_case(oc, args.steps, args.warmup, flush)
         other[f"cfg{c}"] = summarise(oc, ot, peak)
         log(f"cfg{c}: {other[f'cfg{c}']['us_per_step']} us/step, {other[f'cfg{c}']['step_GBps']} GB/s")
+        oc.free()
+        del oc
+        torch.cuda.empty_cache()
+    if "5" in [str(c) for c in others]:
+        # the int8 workload's shapes with an int4 cache (the other quantised KV format)
+        oc = Case(5, None, torch, pa, perfmodel, kv_dtype="i4", name="int4kv-gqa-append")
+        log("timing cfg5 with an int4 cache")
+        ot = time_case(oc, args.steps, args.warmup, flush)
+        other["cfg5-int4"] = summarise(oc, ot, peak)
+        log(f"cfg5-int4: {other['cfg5-int4']['us_per_step']} us/step, {other['cfg5-int4']['step_GBps']} GB/s")
         oc.free()
         del oc
         torch.cuda.empty_cache()

@@ -35,16 +35,20 @@
  *   block ids, and no floating-point atomics are used: results are bitwise
  *   reproducible run to run and invariant under relabelling of blocks.
  *
- * Cache layout (x = elements per 16 bytes: fp32 4, bf16 8, int8 16)
+ * Cache layout (x = elements per storage vector: fp32 4, bf16 8, int8 16 in
+ * 16 bytes; int4 16 codes in 8 bytes)
  * -----------------------------------------------------------------
  *   k_cache  [num_blocks][num_kv_heads][head_dim / x][block_size][x]
  *   v_cache  [num_blocks][num_kv_heads][block_size / x][head_dim][x]
- *   k_scale, v_scale (int8 caches only): fp16 [num_blocks][num_kv_heads][block_size]
+ *   k_scale, v_scale (int8 / int4 caches only): fp16 [num_blocks][num_kv_heads][block_size]
  * K of (block pb, kv head h, in-block offset t, channel d) is
  * k_cache[pb][h][d / x][slot(t)][d % x] with slot(t) = t for fp32 and int8
  * caches and, for bf16 caches, t with its bits 2 and 3 exchanged (offsets
  * 0-3, 8-11, 4-7, 12-15 in every group of 16).  V of (pb, h, t, d) is
- * v_cache[pb][h][t / x][d][t % x].  Scales are indexed by t.
+ * v_cache[pb][h][t / x][d][t % x].  Scales are indexed by t.  int4 caches
+ * hold two 4-bit two's-complement codes per byte, element 2i of a vector in
+ * the low nibble of byte i and element 2i + 1 in the high nibble (INT4 KV
+ * cache: page "LLM推理优化", section 1.3; the packing is this library's).
  * Each (block, kv head) owns block_size * head_dim contiguous elements of
  * each pool, so with one kv head block pb starts at element
  * pb * block_size * head_dim, the address the pages' kernel sketch forms.
@@ -77,19 +81,19 @@ typedef enum {
   PA_ERR_INVALID_BLOCK = 8  /* block manager: a block id out of range or not in use (nothing changed) */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_I4 = 3 } pa_dtype;
 
 /* Descriptor of one paged KV cache (one layer).  Pointers are device pointers. */
 typedef struct pa_kv_cache {
   void *k_cache;        /* see layout above; 16-byte aligned */
   void *v_cache;        /* see layout above; 16-byte aligned */
-  void *k_scale;        /* fp16, int8 caches only (else NULL); 16-byte aligned */
-  void *v_scale;        /* fp16, int8 caches only (else NULL); 16-byte aligned */
+  void *k_scale;        /* fp16, int8 / int4 caches only (else NULL); 16-byte aligned */
+  void *v_scale;        /* fp16, int8 / int4 caches only (else NULL); 16-byte aligned */
   int32_t num_blocks;   /* blocks in the pool, >= 1 */
   int32_t num_kv_heads; /* >= 1 */
   int32_t block_size;   /* tokens per block: 16, 32 or 64 */
   int32_t head_dim;     /* 64 or 128 */
-  pa_dtype kv_dtype;    /* PA_F32, PA_BF16 or PA_I8 */
+  pa_dtype kv_dtype;    /* PA_F32, PA_BF16, PA_I8 or PA_I4 */
 } pa_kv_cache;
 
 /*
@@ -103,13 +107,15 @@ typedef struct pa_kv_cache {
  *
  *   key, value    [num_tokens][num_kv_heads][head_dim], src_dtype, 16-byte aligned
  *   slot_mapping  int32 [num_tokens], 4-byte aligned
- *   src_dtype     PA_F32 for an fp32 cache; PA_BF16 for bf16 and int8 caches
+ *   src_dtype     PA_F32 for an fp32 cache; PA_BF16 for bf16, int8 and int4 caches
  *
  * fp32/bf16 caches store the source bits unchanged.  int8 caches (INT8
  * KV-cache quantisation: page "字节跳动 AI Infra (2)", optimisation table;
  * page "LLM推理优化", section 1.3) store per (token, kv head) the fp16 scale
  * s = fp16_rne(fp32(max|x| / 127)) and codes rint_even(fp32(x / s))
- * clamped to [-127, 127] (all codes 0 when s is 0).  Bit-exact.
+ * clamped to [-127, 127] (all codes 0 when s is 0).  int4 caches (page
+ * "LLM推理优化", section 1.3, names INT4 beside INT8) do the same with
+ * s = fp16_rne(fp32(max|x| / 7)) and codes clamped to [-7, 7].  Bit-exact.
  * Preconditions (device data): slots of one call are distinct; slots
  * >= num_blocks * block_size are skipped.  num_tokens == 0 is a no-op.
  */
@@ -134,7 +140,7 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_
  *   context_lens  int32 [num_seqs]
  *   out           [num_seqs][num_heads][head_dim], out_dtype, 16-byte aligned
  *   (q, kv, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16|F32),
- *                        (BF16, I8, BF16|F32)
+ *                        (BF16, I8, BF16|F32), (BF16, I4, BF16|F32)
  * Accumulation is fp32; bf16 outputs are the round-to-nearest-even of the
  * fp32 result.  Tokens at positions >= L of the last block are never used,
  * whatever they hold (NaN included).
@@ -229,7 +235,7 @@ pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_se
  * into B6', a copy of B6; page "LLM推理优化", section 3.2).  For each
  * i < num_pairs, block block_pairs[2i] (source) is copied to block
  * block_pairs[2i + 1] (destination): every K and V element of every kv head
- * and, for int8 caches, every scale.
+ * and, for int8 and int4 caches, every scale.
  *
  *   cache        the pool (any dtype)
  *   block_pairs  int32 [num_pairs][2] (source, destination), device, 4-byte aligned
@@ -250,7 +256,7 @@ pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, i
  * "vLLM框架是怎么做推理加速的", section 2 and its second follow-up).  For
  * each i < num_pairs, block block_pairs[2i] of `src` is copied to block
  * block_pairs[2i + 1] of `dst`: every K and V element of every kv head and,
- * for int8 caches, every scale.  A block's contents do not depend on where
+ * for int8 and int4 caches, every scale.  A block's contents do not depend on where
  * it lives: after swapping out and back in under new ids (and rewriting the
  * block table) a sequence decodes bit for bit as before.
  *

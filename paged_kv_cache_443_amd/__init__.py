@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PA_BF16, PA_F32, PA_I8, PaKvCache
+from ._lib import PA_BF16, PA_F32, PA_I4, PA_I8, PaKvCache
 
 __all__ = [
     "PAError",
@@ -35,8 +35,9 @@ __all__ = [
 ]
 
 _DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
-_KV_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+_KV_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8}
 _ELEM = {"f32": 4, "bf16": 2, "i8": 1}
+_QUANT = ("i8", "i4")
 
 
 class PAError(RuntimeError):
@@ -92,14 +93,19 @@ class KVCache:
     num_kv_heads: int
     block_size: int
     head_dim: int
-    kv_dtype: str  # "f32" | "bf16" | "i8"
+    kv_dtype: str  # "f32" | "bf16" | "i8" | "i4"
 
     @property
     def x(self) -> int:
-        return 16 // _ELEM[self.kv_dtype]
+        """Elements per storage vector (int4: 16 codes in 8 bytes)."""
+        return 16 if self.kv_dtype == "i4" else 16 // _ELEM[self.kv_dtype]
 
     @staticmethod
     def shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str):
+        if kv_dtype == "i4":  # uint8 pools, two codes per byte
+            return ((num_blocks, num_kv_heads, head_dim // 16, block_size, 8),
+                    (num_blocks, num_kv_heads, block_size // 16, head_dim, 8),
+                    (num_blocks, num_kv_heads, block_size))
         x = 16 // _ELEM[kv_dtype]
         return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
                 (num_blocks, num_kv_heads, block_size // x, head_dim, x),
@@ -116,7 +122,7 @@ class KVCache:
         k = torch.empty(ks, dtype=dt, device=device, pin_memory=pin)
         v = torch.empty(vs, dtype=dt, device=device, pin_memory=pin)
         sk = sv = None
-        if kv_dtype == "i8":
+        if kv_dtype in _QUANT:
             sk = torch.empty(ss, dtype=torch.float16, device=device, pin_memory=pin)
             sv = torch.empty(ss, dtype=torch.float16, device=device, pin_memory=pin)
         return cls(k, v, sk, sv, num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
@@ -128,12 +134,12 @@ class KVCache:
         dt = _KV_TORCH[self.kv_dtype]
         _need(self.k_cache, "k_cache", dt, ks, host_ok)
         _need(self.v_cache, "v_cache", dt, vs, host_ok)
-        if self.kv_dtype == "i8":
+        if self.kv_dtype in _QUANT:
             _need(self.k_scale, "k_scale", torch.float16, ss, host_ok)
             _need(self.v_scale, "v_scale", torch.float16, ss, host_ok)
         return PaKvCache(_ptr(self.k_cache), _ptr(self.v_cache), _ptr(self.k_scale), _ptr(self.v_scale),
                          self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim,
-                         {"f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8}[self.kv_dtype])
+                         {"f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8, "i4": PA_I4}[self.kv_dtype])
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, cache: KVCache) -> None:

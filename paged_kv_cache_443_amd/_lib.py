@@ -22,6 +22,7 @@ PA_ERR_INVALID_BLOCK = 8
 PA_F32 = 0
 PA_BF16 = 1
 PA_I8 = 2
+PA_I4 = 3
 
 EXPORTED = (
     "pa_reshape_and_cache",

@@ -76,7 +76,7 @@ pa_status launch(pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stre
 pa_status launch_block_copies(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs,
                               int32_t num_pairs, hipStream_t stream) {
   if (static_cast<int64_t>(num_pairs) * src->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
-  static const int32_t kElem[] = {4, 2, 1};  // PA_F32, PA_BF16, PA_I8
+  static const int32_t kElemBits[] = {32, 16, 8, 4};  // PA_F32, PA_BF16, PA_I8, PA_I4
   pa::CopyParams p{};
   p.src_k = src->k_cache;
   p.src_v = src->v_cache;
@@ -92,7 +92,7 @@ pa_status launch_block_copies(const pa_kv_cache *src, const pa_kv_cache *dst, co
   p.src_blocks = src->num_blocks;
   p.dst_blocks = dst->num_blocks;
   p.block_size = src->block_size;
-  p.tile_bytes = static_cast<size_t>(src->block_size) * src->head_dim * kElem[src->kv_dtype];
+  p.tile_bytes = static_cast<size_t>(src->block_size) * src->head_dim * kElemBits[src->kv_dtype] / 8;
   return from_hip(pa::launch_copy_blocks(p, stream));
 }
 

@@ -7,8 +7,15 @@
 // "字节跳动 AI Infra (2)", optimisation table; page "LLM推理优化", section 1.3)
 // take per (token, kv head) the fp16 scale fp16_rne(fp32(max|x| / 127)) and
 // codes rint_even(fp32(x / scale)) clamped to [-127, 127], all zero when the
-// scale is zero.  The divisions are IEEE fp32 (the compiler's default
+// scale is zero; int4 caches (page "LLM推理优化", section 1.3) the same with
+// 7 in place of 127.  The divisions are IEEE fp32 (the compiler's default
 // correctly rounded division), so the result is bit-exact.
+//
+// int4 stores two codes per byte.  A K byte holds two channels of one token
+// (one lane's pair, or two neighbouring lanes' codes), so it is written
+// whole.  A V byte holds one channel of two neighbouring tokens, which one
+// call may write from two work-groups: each nibble is replaced with a pair
+// of 32-bit atomic AND / OR operations, so neither write can undo the other.
 //
 // Cache layout as documented in pa.h (bf16 K tiles store offsets in the
 // bit-2/3-exchanged slot order).
@@ -59,10 +66,10 @@ constexpr int kAppendWaves = 4;
 // l owns channels PER*l .. PER*l + PER - 1, which are adjacent in a K tile
 // (one store per lane) and X elements apart in a V tile.  The source rows are
 // loaded alongside the slot, so the only dependent access is the cache write.
-template <int KIND, int D, int BS>  // KIND: 0 fp32, 1 bf16, 2 int8
+template <int KIND, int D, int BS>  // KIND: 0 fp32, 1 bf16, 2 int8, 3 int4
 __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(AppendParams p) {
   constexpr int PER = D / 64;
-  constexpr int X = KIND == 0 ? 4 : (KIND == 1 ? 8 : 16);
+  constexpr int X = KIND == 0 ? 4 : (KIND == 1 ? 8 : 16);  // elements per storage vector
   typedef typename std::conditional<KIND == 0, float, uint16_t>::type Src;
   const int lane = threadIdx.x & 63;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * kAppendWaves + (threadIdx.x >> 6);
@@ -89,6 +96,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(AppendParams 
 #pragma unroll
       for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = vv.e[k];
     } else {
+      constexpr float kQmax = KIND == 2 ? 127.0f : 7.0f;
       int8_t *kc = static_cast<int8_t *>(p.k_cache);
       int8_t *vc = static_cast<int8_t *>(p.v_cache);
 #pragma unroll
@@ -102,23 +110,48 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_kernel(AppendParams 
           amax = fmaxf(amax, fabsf(xv[k]));
         }
         amax = wave_max(amax);
-        const uint16_t s16 = float_to_half_bits(amax / 127.0f);
+        const uint16_t s16 = float_to_half_bits(amax / kQmax);
         const float sf = half_bits_to_float(s16);
         Pack<int8_t, PER> q;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
           float qf = 0.f;
-          if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -127.f), 127.f);
+          if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -kQmax), kQmax);
           q.e[k] = static_cast<int8_t>(static_cast<int>(qf));
         }
-        if (which == 0) {
-          store_pack<int8_t, PER>(kc + k_off<D, BS, X>(tile, o, d0), q);
-          if (lane == 0) p.k_scale[tile * BS + o] = s16;
-        } else {
+        if constexpr (KIND == 2) {
+          if (which == 0) {
+            store_pack<int8_t, PER>(kc + k_off<D, BS, X>(tile, o, d0), q);
+          } else {
 #pragma unroll
-          for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = q.e[k];
-          if (lane == 0) p.v_scale[tile * BS + o] = s16;
+            for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = q.e[k];
+          }
+        } else if (which == 0) {
+          // K: channels 2i, 2i + 1 of this token share byte i of its vector
+          uint32_t byte;
+          if constexpr (PER == 2) {
+            byte = (static_cast<uint32_t>(q.e[0]) & 0xfu) | ((static_cast<uint32_t>(q.e[1]) & 0xfu) << 4);
+          } else {
+            const int other = __shfl_xor(static_cast<int>(q.e[0]), 1);  // the neighbouring channel
+            byte = (static_cast<uint32_t>(q.e[0]) & 0xfu) | ((static_cast<uint32_t>(other) & 0xfu) << 4);
+          }
+          if (PER == 2 || (lane & 1) == 0) {
+            const size_t e = k_off<D, BS, X>(tile, o, d0);  // element index; two per byte
+            reinterpret_cast<uint8_t *>(kc)[e / 2] = static_cast<uint8_t>(byte);
+          }
+        } else {
+          // V: channel d's byte holds tokens o & ~1 (low nibble) and o | 1
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const size_t e = v_off<D, BS, X>(tile, o, d0 + k);
+            const size_t byte_at = e / 2;
+            uint32_t *word = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(vc) + (byte_at & ~size_t(3)));
+            const int shift = 8 * static_cast<int>(byte_at & 3) + 4 * (o & 1);
+            atomicAnd(word, ~(0xfu << shift));
+            atomicOr(word, (static_cast<uint32_t>(q.e[k]) & 0xfu) << shift);
+          }
         }
+        if (lane == 0) (which == 0 ? p.k_scale : p.v_scale)[tile * BS + o] = s16;
       }
     }
   }
@@ -152,6 +185,7 @@ hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s
     case PA_F32: return launch_d<0>(p, s);
     case PA_BF16: return launch_d<1>(p, s);
     case PA_I8: return launch_d<2>(p, s);
+    case PA_I4: return launch_d<3>(p, s);
   }
   return hipErrorInvalidValue;
 }

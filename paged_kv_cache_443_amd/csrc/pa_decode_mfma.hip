@@ -42,20 +42,38 @@
 namespace pa {
 namespace {
 
+// KV cache storage kinds (template argument KV).
+constexpr int kBf16 = 0;
+constexpr int kInt8 = 1;
+constexpr int kInt4 = 2;
+template <int KV>
+constexpr bool kQuant = KV != kBf16;  // codes + fp16 scales per (token, kv head)
+
+// One K/V storage vector: 16 bytes (8 bf16 or 16 int8 values), or 8 bytes
+// of 16 int4 codes.  int4 keeps the int8 lane mapping with half the bytes.
+template <int KV>
+struct KvVec {
+  typedef u32x4 T;
+};
+template <>
+struct KvVec<kInt4> {
+  typedef u32x2 T;
+};
+
 // Sequences a persistent split launch can index from LDS (4 bytes each).
 constexpr int kMaxPersistentSeqs = 4096;
 // Sequences a single-pass launch ranks by length in every work-group (the
 // ranking costs num_seqs^2 / threads LDS reads per work-group).
 constexpr int kMaxLptSeqs = 512;
 
-template <bool I8, int D>
+template <int KV, int D>
 struct Tile {
-  static constexpr int X = I8 ? 16 : 8;      // elements per 16 bytes
-  static constexpr int TPL = I8 ? 16 : 8;    // tokens per lane group per chunk
+  static constexpr int X = kQuant<KV> ? 16 : 8;    // elements per storage vector
+  static constexpr int TPL = kQuant<KV> ? 16 : 8;  // tokens per lane group per chunk
   static constexpr int CT = 4 * TPL;         // tokens per chunk
   static constexpr int NQ = CT / 16;         // QK row groups per chunk
   static constexpr int NS = D / 32;          // MFMA k-steps over head_dim
-  static constexpr int NKL = D / (4 * X);    // 16-byte K loads per lane per row group
+  static constexpr int NKL = D / (4 * X);    // K vector loads per lane per row group
   static constexpr int ND = D / 16;          // 16-channel blocks of the output
   static constexpr int NR = TPL / 8;         // PV products per channel block
 };
@@ -64,15 +82,15 @@ struct Tile {
 // K of the next chunk is loaded while this chunk's softmax still runs, so
 // everything the softmax reads besides the scores (the int8 scales) travels
 // with the V buffer, which stays live until the chunk is finished.
-template <bool I8, int D>
+template <int KV, int D>
 struct KBuf {
-  u32x4 k[Tile<I8, D>::NQ][Tile<I8, D>::NKL];
+  typename KvVec<KV>::T k[Tile<KV, D>::NQ][Tile<KV, D>::NKL];
 };
-template <bool I8, int D>
+template <int KV, int D>
 struct VBuf {
-  u32x4 ks[I8 ? 2 : 1];  // int8: this lane group's 16 K scales
-  u32x4 vs[I8 ? 2 : 1];  // int8: this lane group's 16 V scales
-  u32x4 v[Tile<I8, D>::ND];
+  u32x4 ks[kQuant<KV> ? 2 : 1];  // int8 / int4: this lane group's 16 K scales
+  u32x4 vs[kQuant<KV> ? 2 : 1];  // int8 / int4: this lane group's 16 V scales
+  typename KvVec<KV>::T v[Tile<KV, D>::ND];
 };
 
 // Physical block ids this lane needs for one chunk (its K rows and its V tokens).
@@ -80,11 +98,11 @@ struct Ids {
   int32_t k, v;
 };
 
-template <bool I8, int D, int BS>
+template <int KV, int D, int BS>
 struct Ctx {
-  const u32x4 *kpool;
-  const u32x4 *vpool;
-  const u32x4 *kscale;   // int8 only: fp16 scales viewed as 16-byte vectors
+  const typename KvVec<KV>::T *kpool;
+  const typename KvVec<KV>::T *vpool;
+  const u32x4 *kscale;   // int8 / int4 only: fp16 scales viewed as 16-byte vectors
   const u32x4 *vscale;
   const int32_t *tbl;    // LDS copy of the block-table window
   int32_t lb0;           // logical block of tbl[0]
@@ -101,11 +119,11 @@ struct Ctx {
 // K/V tile loads.  Tiles are read once per step and streamed past the caches
 // (non-temporal) wherever a load instruction covers whole 128-byte lines, so
 // that nothing is fetched twice: every bf16 load (K slot order above) and
-// every V load.  int8 K row groups cover quarter lines (four tokens of each
-// of four blocks); the four row-group loads of a chunk share those lines,
-// so int8 K uses ordinary loads and the lines stay in L2 between them.
-template <bool STREAM>
-__device__ __forceinline__ u32x4 load_tile(const u32x4 *ptr) {
+// every V load.  int8 (int4) K row groups cover quarter (eighth) lines; the
+// four row-group loads of a chunk share those lines, so quantised K uses
+// ordinary loads and the lines stay in L2 between them.
+template <bool STREAM, typename V>
+__device__ __forceinline__ V load_tile(const V *ptr) {
   if constexpr (STREAM)
     return __builtin_nontemporal_load(ptr);
   else
@@ -113,9 +131,9 @@ __device__ __forceinline__ u32x4 load_tile(const u32x4 *ptr) {
 }
 
 // Block ids of chunk starting at position cs, read from the LDS table window.
-template <bool I8, int D, int BS>
-__device__ __forceinline__ Ids read_ids(const Ctx<I8, D, BS> &x, int cs) {
-  using T = Tile<I8, D>;
+template <int KV, int D, int BS>
+__device__ __forceinline__ Ids read_ids(const Ctx<KV, D, BS> &x, int cs) {
+  using T = Tile<KV, D>;
   const int lbk = min((cs + T::TPL * (x.m >> 2)) / BS, x.nbv - 1) - x.lb0;
   const int lbv = min((cs + T::TPL * x.j) / BS, x.nbv - 1) - x.lb0;
   Ids r;
@@ -128,28 +146,28 @@ __device__ __forceinline__ Ids read_ids(const Ctx<I8, D, BS> &x, int cs) {
 // NT: non-temporal loads where they pay (every unit reads its K/V once);
 // ordinary loads when several row groups of a unit read the same lines, so
 // that the later reads hit the cache.
-template <bool NT, bool I8, int D, int BS>
-__device__ __forceinline__ void issue_k(KBuf<I8, D> &kb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
-  using T = Tile<I8, D>;
+template <bool NT, int KV, int D, int BS>
+__device__ __forceinline__ void issue_k(KBuf<KV, D> &kb, const Ctx<KV, D, BS> &x, int cs, Ids id) {
+  using T = Tile<KV, D>;
   const size_t ktile = static_cast<size_t>(static_cast<uint32_t>(id.k) * static_cast<uint32_t>(x.hkv) + x.kvh);
-  // K: [tile][D/X][BS] 16-byte vectors
-  const u32x4 *kp = x.kpool + ktile * (D / T::X) * BS;
+  // K: [tile][D/X][BS] storage vectors
+  const typename KvVec<KV>::T *kp = x.kpool + ktile * (D / T::X) * BS;
 #pragma unroll
   for (int q = 0; q < T::NQ; ++q) {
     const int off = (cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3)) % BS;
-    const int ok = I8 ? off : bf16_k_slot(off);  // lanes m % 8 read one 128-byte run
+    const int ok = kQuant<KV> ? off : bf16_k_slot(off);  // bf16: lanes m % 8 read one 128-byte run
 #pragma unroll
-    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_tile<NT && !I8>(kp + (4 * s + x.j) * BS + ok);
+    for (int s = 0; s < T::NKL; ++s) kb.k[q][s] = load_tile<NT && !kQuant<KV>>(kp + (4 * s + x.j) * BS + ok);
   }
 }
 
-template <bool NT, bool I8, int D, int BS>
-__device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x, int cs, Ids id) {
-  using T = Tile<I8, D>;
+template <bool NT, int KV, int D, int BS>
+__device__ __forceinline__ void issue_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x, int cs, Ids id) {
+  using T = Tile<KV, D>;
   const size_t vtile = static_cast<size_t>(static_cast<uint32_t>(id.v) * static_cast<uint32_t>(x.hkv) + x.kvh);
-  // V: [tile][BS/X][D] 16-byte vectors
+  // V: [tile][BS/X][D] storage vectors
   const int ov = (cs + T::TPL * x.j) % BS;
-  if constexpr (I8) {
+  if constexpr (kQuant<KV>) {
     // scales first: the softmax needs them before PV needs the V data
     const size_t sidx = (vtile * BS + ov) / 8;
     vb.ks[0] = x.kscale[sidx];
@@ -157,44 +175,47 @@ __device__ __forceinline__ void issue_v(VBuf<I8, D> &vb, const Ctx<I8, D, BS> &x
     vb.vs[0] = x.vscale[sidx];
     vb.vs[1] = x.vscale[sidx + 1];
   }
-  const u32x4 *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
+  const typename KvVec<KV>::T *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<NT>(vp + 16 * n);
 }
 
-template <bool I8, int D>
+template <int KV, int D>
 struct Scores {
-  f32x4 s[Tile<I8, D>::NQ];  // row group q: tokens TPL*j + 4q + i of head m
+  f32x4 s[Tile<KV, D>::NQ];  // row group q: tokens TPL*j + 4q + i of head m
 };
-template <bool I8, int D>
+template <int KV, int D>
 struct Probs {
-  float p[Tile<I8, D>::NQ * 4];  // tokens TPL*j + e of head m
+  float p[Tile<KV, D>::NQ * 4];  // tokens TPL*j + e of head m
 };
-template <bool I8, int D>
+template <int KV, int D>
 struct QOp {
-  bf16x8 q[Tile<I8, D>::NS];  // B operand of the QK product
+  bf16x8 q[Tile<KV, D>::NS];  // B operand of the QK product
 };
 
-template <bool I8, int D>
+template <int KV, int D>
 struct State {
-  f32x4 acc[Tile<I8, D>::ND];  // O^T[16n + 4j + i][head m]
+  f32x4 acc[Tile<KV, D>::ND];  // O^T[16n + 4j + i][head m]
   float m_run;                 // running max of log2-domain scores (head m)
   float l_run;                 // this lane's share of the running sum
 };
 
 // Scores of one chunk: S^T = K Q^T (row group q holds tokens TPL*j + 4q + i).
-template <bool I8, int D>
-__device__ __forceinline__ void qk(Scores<I8, D> &S, const KBuf<I8, D> &kb, const QOp<I8, D> &qop) {
-  using T = Tile<I8, D>;
+template <int KV, int D>
+__device__ __forceinline__ void qk(Scores<KV, D> &S, const KBuf<KV, D> &kb, const QOp<KV, D> &qop) {
+  using T = Tile<KV, D>;
 #pragma unroll
   for (int q = 0; q < T::NQ; ++q) {
     S.s[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < T::NS; ++s) {
       bf16x8 a;
-      if constexpr (I8) {
+      if constexpr (KV == kInt8) {
         const u32x4 w = kb.k[q][s >> 1];
         a = (s & 1) ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else if constexpr (KV == kInt4) {
+        const u32x2 w = kb.k[q][s >> 1];
+        a = i4x8_to_bf16x8((s & 1) ? w[1] : w[0]);
       } else {
         a = __builtin_bit_cast(bf16x8, kb.k[q][s]);
       }
@@ -209,10 +230,10 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return half_bits_to_float
 // Online-softmax update for one chunk; returns the probabilities (V scale
 // folded in for int8) of this lane's tokens TPL*j + e.  TAIL: positions may
 // reach t1.
-template <bool I8, int D, bool TAIL, bool CAUSAL = false>
-__device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, const VBuf<I8, D> &vb, Probs<I8, D> &P,
+template <int KV, int D, bool TAIL, bool CAUSAL = false>
+__device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, const VBuf<KV, D> &vb, Probs<KV, D> &P,
                                         int tok0, int t1, float scale_log2) {
-  using T = Tile<I8, D>;
+  using T = Tile<KV, D>;
   float mloc = -INFINITY;
 #pragma unroll
   for (int q = 0; q < T::NQ; ++q) {
@@ -220,7 +241,7 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * q + i;
       float sv;
-      if constexpr (I8) {
+      if constexpr (kQuant<KV>) {
         const uint32_t kw = vb.ks[e >> 3][(e >> 1) & 3];
         sv = S.s[q][i] * (scale_log2 * ((e & 1) ? half_hi(kw) : half_lo(kw)));
       } else {
@@ -247,7 +268,7 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
       const int e = 4 * q + i;
       const float pe = fast_exp2(S.s[q][i] - m_ref);
       psum += pe;
-      if constexpr (I8) {
+      if constexpr (kQuant<KV>) {
         const uint32_t vw = vb.vs[e >> 3][(e >> 1) & 3];
         float f = pe * ((e & 1) ? half_hi(vw) : half_lo(vw));  // V scale folded into P
         if constexpr (TAIL) f = (tok0 + e < t1) ? f : 0.f;     // scale of an unused slot may be NaN
@@ -263,11 +284,11 @@ __device__ __forceinline__ void softmax(State<I8, D> &st, Scores<I8, D> &S, cons
 }
 
 // O^T += V^T P^T, P split into bf16 hi + lo parts.
-template <bool I8, int D, bool TAIL>
-__device__ __forceinline__ void pv_update(State<I8, D> &st, VBuf<I8, D> &vb, const Probs<I8, D> &P, int tok0,
+template <int KV, int D, bool TAIL>
+__device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, const Probs<KV, D> &P, int tok0,
                                           int t1) {
-  using T = Tile<I8, D>;
-  if constexpr (TAIL && !I8) {
+  using T = Tile<KV, D>;
+  if constexpr (TAIL && !kQuant<KV>) {
     // V of positions >= t1 may hold NaN: zero it (0 * NaN would poison the sum)
     uint32_t keep[4];
 #pragma unroll
@@ -291,9 +312,12 @@ __device__ __forceinline__ void pv_update(State<I8, D> &st, VBuf<I8, D> &vb, con
 #pragma unroll
     for (int n = 0; n < T::ND; ++n) {
       bf16x8 a;
-      if constexpr (I8) {
+      if constexpr (KV == kInt8) {
         const u32x4 w = vb.v[n];
         a = r ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else if constexpr (KV == kInt4) {
+        const u32x2 w = vb.v[n];
+        a = i4x8_to_bf16x8(r ? w[1] : w[0]);
       } else {
         a = __builtin_bit_cast(bf16x8, vb.v[n]);
       }
@@ -339,21 +363,21 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-template <bool I8, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true>
-__device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<I8, D> &vb,
-                                        const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop, int cs, int cn, Ids idn,
+template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true>
+__device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<KV, D> &vb,
+                                        const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop, int cs, int cn, Ids idn,
                                         float scale_log2) {
-  using T = Tile<I8, D>;
-  Scores<I8, D> S;
-  Probs<I8, D> P;
-  qk<I8, D>(S, kb, qop);
+  using T = Tile<KV, D>;
+  Scores<KV, D> S;
+  Probs<KV, D> P;
+  qk<KV, D>(S, kb, qop);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_k<NT>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
-  softmax<I8, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2);
-  pv_update<I8, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2);
+  pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_v<NT>(vb, x, cn, idn);
@@ -363,12 +387,12 @@ __device__ __forceinline__ void consume(State<I8, D> &st, KBuf<I8, D> &kb, VBuf<
 
 // A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
 // while the previous one is computed.
-template <bool I8, int D, int BS, int NW, bool CAUSAL = false, bool NT = true>
-__device__ __forceinline__ void stream_chunks(State<I8, D> &st, const Ctx<I8, D, BS> &x, const QOp<I8, D> &qop,
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, bool NT = true>
+__device__ __forceinline__ void stream_chunks(State<KV, D> &st, const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop,
                                                 int c0, int n, float scale_log2) {
-  constexpr int STEP = NW * Tile<I8, D>::CT;
-  KBuf<I8, D> kb;
-  VBuf<I8, D> vb;
+  constexpr int STEP = NW * Tile<KV, D>::CT;
+  KBuf<KV, D> kb;
+  VBuf<KV, D> vb;
   int cs = c0;
   const Ids ids = read_ids(x, cs);
   issue_k<NT>(kb, x, cs, ids);
@@ -376,13 +400,13 @@ __device__ __forceinline__ void stream_chunks(State<I8, D> &st, const Ctx<I8, D,
   for (int k = 0; k + 1 < n; ++k) {
     const int cn = cs + STEP;
     // a causal unit's last new tokens are hidden from its earlier query rows
-    if (CAUSAL && cs + Tile<I8, D>::CT > x.t1_min)
-      consume<I8, D, BS, true, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+    if (CAUSAL && cs + Tile<KV, D>::CT > x.t1_min)
+      consume<KV, D, BS, true, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     else
-      consume<I8, D, BS, false, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
+      consume<KV, D, BS, false, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     cs = cn;
   }
-  consume<I8, D, BS, true, false, CAUSAL, NT>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
+  consume<KV, D, BS, true, false, CAUSAL, NT>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
 }
 
 // One unit of work: (sequence b, kv head x query-head group hx[, partition]).
@@ -399,9 +423,9 @@ __device__ __forceinline__ void stream_chunks(State<I8, D> &st, const Ctx<I8, D,
 // group w % R and takes every (NW / R)-th chunk of that group's tokens, so
 // the R groups walk the same K/V chunks at about the same time and all but
 // the first read of each line come from the cache.
-template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
-  using T = Tile<I8, D>;
+  using T = Tile<KV, D>;
   static_assert(NW % R == 0, "row groups must divide the wavefronts");
   constexpr int NWT = NW / R;  // wavefronts sharing one row group's tokens
   const int lane = threadIdx.x & 63;
@@ -440,14 +464,14 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   // the work-group, and no barrier has been reached)
   if (split && t0 >= L) return;
 
-  Ctx<I8, D, BS> x;
+  Ctx<KV, D, BS> x;
   x.m = lane & 15;
   x.j = lane >> 4;
   x.kvh = kvh;
   x.hkv = p.num_kv_heads;
   x.num_blocks_m1 = p.num_blocks - 1;
-  x.kpool = static_cast<const u32x4 *>(p.k_cache);
-  x.vpool = static_cast<const u32x4 *>(p.v_cache);
+  x.kpool = static_cast<const typename KvVec<KV>::T *>(p.k_cache);
+  x.vpool = static_cast<const typename KvVec<KV>::T *>(p.v_cache);
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm.tbl;
@@ -467,7 +491,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   x.nbv = (x.t1 + BS - 1) / BS;
 
   // ---- query operand (B of the QK product): row r0 + m -------------------------
-  QOp<I8, D> qop;
+  QOp<KV, D> qop;
   {
     const int r = r0 + x.m;
     const int qi = CAUSAL ? r / p.group : 0;  // single-token rows are heads of query token 0
@@ -482,14 +506,14 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     x.t1_min = L - nq + r0 / p.group + 1;
 #pragma unroll
     for (int s = 0; s < T::NS; ++s) {
-      const int d0 = I8 ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
+      const int d0 = kQuant<KV> ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (qvalid) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
       qop.q[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  State<I8, D> st;
+  State<KV, D> st;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = -INFINITY;
@@ -512,7 +536,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int wew = R == 1 ? we : min(we, x.t1);
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
-    if (n > 0) stream_chunks<I8, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
+    if (n > 0) stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
@@ -578,7 +602,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -621,7 +645,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<I8, D, BS, NW, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<KV, D, BS, NW, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -632,7 +656,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // a piece index then maps to its sequence by binary search.  No work-group is
 // spent on a partition past the end of its sequence, and the pieces are of
 // near-equal size, so a static stride balances the work.
-template <bool I8, int D, int BS, int NW>
+template <int KV, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -685,18 +709,18 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
     }
     const int local = piece - sm.first[lo];
     const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
-    if (n_b > 0) run_unit<I8, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
+    if (n_b > 0) run_unit<KV, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
   }
 }
 
 // Split pass: persistent when the sequences' piece offsets fit in LDS,
 // else one work-group per (unit, partition).
-template <bool I8, int D, int BS, int NW>
+template <int KV, int D, int BS, int NW>
 hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   const int rows = p.rows_per_group;
   if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
-    const auto kern = decode_split_persistent_kernel<I8, D, BS, NW>;
+    const auto kern = decode_split_persistent_kernel<KV, D, BS, NW>;
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -710,7 +734,7 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   }
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_num_partitions;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
                      lds, s, p);
   return hipGetLastError();
 }
@@ -720,14 +744,14 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
 // than one work-group, so that another one streams while a work-group ranks
 // (measured: +3 points for four-wave int8 units; with one eight-wave
 // work-group per CU the ranking is dead time and cost 2 points).
-template <bool I8, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
 hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
   p.lpt = (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
   p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, D, BS, NW, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
                      dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
@@ -744,18 +768,18 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
 // 1.1-2.0x and four or eight by 1.3-2.4x).  The choice depends on the launch
 // shape only, so a multi-query launch with one token per sequence is the
 // single-token launch.
-template <bool I8, int D, int BS, int NW, bool CAUSAL>
+template <int KV, int D, int BS, int NW, bool CAUSAL>
 hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
   const int rg = p.head_groups;  // row groups of a (sequence, kv head)
   const int most = p.max_q_len > 1 ? NW : 2;
   int r = 1;
   while (r < rg && r < most) r *= 2;
   switch (r) {
-    case 1: return launch_single<I8, D, BS, NW, CAUSAL, 1>(p, s);
-    case 2: return launch_single<I8, D, BS, NW, CAUSAL, 2>(p, s);
-    case 4: return launch_single<I8, D, BS, NW, CAUSAL, 4>(p, s);
+    case 1: return launch_single<KV, D, BS, NW, CAUSAL, 1>(p, s);
+    case 2: return launch_single<KV, D, BS, NW, CAUSAL, 2>(p, s);
+    case 4: return launch_single<KV, D, BS, NW, CAUSAL, 4>(p, s);
   }
-  return launch_single<I8, D, BS, NW, CAUSAL, (NW >= 8 ? 8 : 4)>(p, s);
+  return launch_single<KV, D, BS, NW, CAUSAL, (NW >= 8 ? 8 : 4)>(p, s);
 }
 
 // Wavefronts per unit.  A single-pass bf16 unit is a whole sequence: eight
@@ -764,36 +788,46 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
 // kernel's register use).  Split pieces are short and int8 units hold twice
 // the tokens per chunk: there four wavefronts and more work-groups per CU
 // measured faster.
-template <bool I8, int D, int BS>
+template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
   const bool causal = p.q_start != nullptr;
-  if constexpr (I8) {
-    if (p.partition_size > 0) return launch_split<I8, D, BS, 4>(p, s);
-    if (causal) return launch_rows<I8, D, BS, 4, true>(p, s);
-    return launch_rows<I8, D, BS, 4, false>(p, s);
+  if constexpr (kQuant<KV>) {
+    if (p.partition_size > 0) return launch_split<KV, D, BS, 4>(p, s);
+    if (causal) return launch_rows<KV, D, BS, 4, true>(p, s);
+    return launch_rows<KV, D, BS, 4, false>(p, s);
   } else {
-    if (p.partition_size > 0) return launch_split<I8, D, BS, 4>(p, s);
-    if (causal) return launch_rows<I8, D, BS, 8, true>(p, s);
-    return launch_rows<I8, D, BS, 8, false>(p, s);
+    if (p.partition_size > 0) return launch_split<KV, D, BS, 4>(p, s);
+    if (causal) return launch_rows<KV, D, BS, 8, true>(p, s);
+    return launch_rows<KV, D, BS, 8, false>(p, s);
   }
 }
 
-template <bool I8, int D>
+template <int KV, int D>
 hipError_t launch_bs(const DecodeParams &p, int bs, hipStream_t s) {
   switch (bs) {
-    case 16: return launch_t<I8, D, 16>(p, s);
-    case 32: return launch_t<I8, D, 32>(p, s);
-    case 64: return launch_t<I8, D, 64>(p, s);
+    case 16: return launch_t<KV, D, 16>(p, s);
+    case 32: return launch_t<KV, D, 32>(p, s);
+    case 64: return launch_t<KV, D, 64>(p, s);
   }
+  return hipErrorInvalidValue;
+}
+
+template <int KV>
+hipError_t launch_kv(const DecodeParams &p, int head_dim, int block_size, hipStream_t s) {
+  if (head_dim == 128) return launch_bs<KV, 128>(p, block_size, s);
+  if (head_dim == 64) return launch_bs<KV, 64>(p, block_size, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s) {
-  const bool i8 = kv_dtype == PA_I8;
-  if (head_dim == 128) return i8 ? launch_bs<true, 128>(p, block_size, s) : launch_bs<false, 128>(p, block_size, s);
-  if (head_dim == 64) return i8 ? launch_bs<true, 64>(p, block_size, s) : launch_bs<false, 64>(p, block_size, s);
+  switch (kv_dtype) {
+    case PA_BF16: return launch_kv<kBf16>(p, head_dim, block_size, s);
+    case PA_I8: return launch_kv<kInt8>(p, head_dim, block_size, s);
+    case PA_I4: return launch_kv<kInt4>(p, head_dim, block_size, s);
+    default: break;
+  }
   return hipErrorInvalidValue;
 }
 

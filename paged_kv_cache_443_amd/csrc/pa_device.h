@@ -9,6 +9,7 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -47,6 +48,20 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     const int sh = (k & 1) * 16;
     const float f0 = static_cast<float>(static_cast<int8_t>((w >> sh) & 0xffu));
     const float f1 = static_cast<float>(static_cast<int8_t>((w >> (sh + 8)) & 0xffu));
+    r[k] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Eight 4-bit two's-complement codes (nibble k = element k, low nibble
+// first) -> eight bf16 values, exactly (|code| <= 8 needs 4 significant bits).
+__device__ __forceinline__ bf16x8 i4x8_to_bf16x8(uint32_t w) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // sign-extend nibbles 2k and 2k+1 by shifting each to the top of a word
+    const float f0 = static_cast<float>(static_cast<int32_t>(w << (28 - 8 * k)) >> 28);
+    const float f1 = static_cast<float>(static_cast<int32_t>(w << (24 - 8 * k)) >> 28);
     r[k] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
   return __builtin_bit_cast(bf16x8, r);

@@ -19,8 +19,9 @@ bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
 
 pa_status check_cache(const pa_kv_cache *c) {
   if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr) return PA_ERR_NULL_PTR;
-  if (c->kv_dtype != PA_F32 && c->kv_dtype != PA_BF16 && c->kv_dtype != PA_I8) return PA_ERR_UNSUPPORTED;
-  const bool want_scales = c->kv_dtype == PA_I8;
+  if (c->kv_dtype != PA_F32 && c->kv_dtype != PA_BF16 && c->kv_dtype != PA_I8 && c->kv_dtype != PA_I4)
+    return PA_ERR_UNSUPPORTED;
+  const bool want_scales = c->kv_dtype == PA_I8 || c->kv_dtype == PA_I4;
   if (want_scales && (c->k_scale == nullptr || c->v_scale == nullptr)) return PA_ERR_NULL_PTR;
   if (!want_scales && (c->k_scale != nullptr || c->v_scale != nullptr)) return PA_ERR_NULL_PTR;
   if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1 || c->head_dim < 1) return PA_ERR_BAD_SHAPE;
@@ -64,7 +65,7 @@ pa_status check_decode_common(const void *q, pa_dtype q_dtype, int32_t num_seqs,
 pa_status check_out(const void *out, pa_dtype q_dtype, pa_dtype kv_dtype, pa_dtype out_dtype) {
   if (out == nullptr) return PA_ERR_NULL_PTR;
   const bool ok = (q_dtype == PA_F32 && kv_dtype == PA_F32 && out_dtype == PA_F32) ||
-                  (q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8) &&
+                  (q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8 || kv_dtype == PA_I4) &&
                    (out_dtype == PA_BF16 || out_dtype == PA_F32));
   if (!ok) return PA_ERR_UNSUPPORTED;
   if (!aligned(out, 16)) return PA_ERR_MISALIGNED;

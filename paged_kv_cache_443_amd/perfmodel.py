@@ -12,7 +12,7 @@ from typing import Iterable, Optional
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "i8": 1}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, vendor figure (no sparsity)
 
@@ -40,7 +40,7 @@ def decode_bytes(context_lens: Iterable[int], *, Hq: int, Hkv: int, D: int, bs: 
     toks = int(L.sum()) - int(shared_tokens)
     e = ELEM_BYTES[kv_dtype]
     kv = toks * Hkv * D * 2 * e
-    if kv_dtype == "i8":
+    if kv_dtype in ("i8", "i4"):
         kv += toks * Hkv * 2 * 2  # fp16 K and V scale per (token, kv head)
     qo = B * Hq * D * (ELEM_BYTES[q_dtype] + ELEM_BYTES[out_dtype])
     tables = int(np.sum((L + bs - 1) // bs)) * 4 + B * 4
@@ -58,7 +58,7 @@ def multi_bytes(context_lens: Iterable[int], query_counts: Iterable[int], *, Hq:
     e = ELEM_BYTES[kv_dtype]
     toks = int(L.sum())
     kv = toks * Hkv * D * 2 * e
-    if kv_dtype == "i8":
+    if kv_dtype in ("i8", "i4"):
         kv += toks * Hkv * 2 * 2
     qo = rows * Hq * D * (ELEM_BYTES[q_dtype] + ELEM_BYTES[out_dtype])
     tables = int(np.sum((L + bs - 1) // bs)) * 4 + len(L) * 4 + (len(L) + 1) * 4
@@ -81,7 +81,7 @@ def append_bytes(num_tokens: int, *, Hkv: int, D: int, kv_dtype: str, src_dtype:
     T = int(num_tokens)
     rd = T * Hkv * D * 2 * ELEM_BYTES[src_dtype] + T * 4
     wr = T * Hkv * D * 2 * ELEM_BYTES[kv_dtype]
-    if kv_dtype == "i8":
+    if kv_dtype in ("i8", "i4"):
         wr += T * Hkv * 2 * 2
     return int(rd + wr)
 

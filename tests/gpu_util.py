@@ -17,7 +17,7 @@ from workloads.device import (DEV, append_tokens, fill_poison, meta, poisoned_ca
 
 gpu_append_tokens = append_tokens
 
-TOL = {"f32": 2e-3, "bf16": 1.5e-2, "i8": 1.5e-2}
+TOL = {"f32": 2e-3, "bf16": 1.5e-2, "i8": 1.5e-2, "i4": 1.5e-2}
 
 
 def say(*a):
@@ -31,18 +31,21 @@ def upload_oracle_cache(oc) -> pa.KVCache:
     if kv == "bf16":
         k = torch.from_numpy(oc.k.view(np.int16)).to(DEV).view(torch.bfloat16)
         v = torch.from_numpy(oc.v.view(np.int16)).to(DEV).view(torch.bfloat16)
+    elif kv == "i4":  # the stored bytes, two codes each
+        k = torch.from_numpy(oc.packed_k()).to(DEV)
+        v = torch.from_numpy(oc.packed_v()).to(DEV)
     else:
         k = torch.from_numpy(oc.k).to(DEV)
         v = torch.from_numpy(oc.v).to(DEV)
     ks = vs = None
-    if kv == "i8":
+    if kv in ("i8", "i4"):
         ks = torch.from_numpy(oc.k_scale).to(DEV)
         vs = torch.from_numpy(oc.v_scale).to(DEV)
     return pa.KVCache(k.contiguous(), v.contiguous(), ks, vs, oc.num_blocks, oc.Hkv, oc.bs, oc.D, kv)
 
 
 def download_cache(c: pa.KVCache):
-    """Host numpy copies of the pools in the oracle's storage dtypes."""
+    """Host numpy copies of the pools in the oracle's storage dtypes (int4: the stored bytes)."""
     if c.kv_dtype == "bf16":
         k = c.k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
         v = c.v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -50,7 +53,7 @@ def download_cache(c: pa.KVCache):
         k = c.k_cache.cpu().numpy()
         v = c.v_cache.cpu().numpy()
     ks = vs = None
-    if c.kv_dtype == "i8":
+    if c.kv_dtype in ("i8", "i4"):
         ks = c.k_scale.cpu().numpy()
         vs = c.v_scale.cpu().numpy()
     return k, v, ks, vs

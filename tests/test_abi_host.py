@@ -9,7 +9,7 @@ import pytest
 
 from paged_kv_cache_443_amd import _lib
 from paged_kv_cache_443_amd._lib import (PA_BF16, PA_ERR_BAD_SHAPE, PA_ERR_BAD_WORKSPACE, PA_ERR_MISALIGNED,
-                                         PA_ERR_NULL_PTR, PA_ERR_UNSUPPORTED, PA_F32, PA_I8, PA_OK, PaKvCache)
+                                         PA_ERR_NULL_PTR, PA_ERR_UNSUPPORTED, PA_F32, PA_I4, PA_I8, PA_OK, PaKvCache)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
@@ -20,7 +20,7 @@ A16 = [A + 0x1000 * i for i in range(1, 16)]
 
 
 def _cache(kv=PA_BF16, nb=8, H=2, bs=16, D=128, k=A16[0], v=A16[1], ks=None, vs=None):
-    if kv == PA_I8 and ks is None:
+    if kv in (PA_I8, PA_I4) and ks is None:
         ks, vs = A16[2], A16[3]
     return PaKvCache(k, v, ks, vs, nb, H, bs, D, kv)
 
@@ -69,6 +69,10 @@ def test_decode_rejections(L):
     assert _decode(L, _cache(k=None)) == PA_ERR_NULL_PTR
     assert _decode(L, _cache(ks=A16[2])) == PA_ERR_NULL_PTR  # scales on a bf16 cache
     assert _decode(L, PaKvCache(A16[0], A16[1], None, None, 8, 2, 16, 128, PA_I8)) == PA_ERR_NULL_PTR  # int8 without scales
+    assert _decode(L, PaKvCache(A16[0], A16[1], None, None, 8, 2, 16, 128, PA_I4)) == PA_ERR_NULL_PTR  # int4 without scales
+    assert _decode(L, _cache(kv=PA_I4), qdt=PA_F32) == PA_ERR_UNSUPPORTED  # f32 q with an int4 cache
+    assert _decode(L, _cache(kv=PA_I4), odt=PA_I4) == PA_ERR_UNSUPPORTED
+    assert _decode(L, _cache(kv=4)) == PA_ERR_UNSUPPORTED  # no such dtype
     assert _decode(L, c, B=-1) == PA_ERR_BAD_SHAPE
     assert _decode(L, c, Hq=0) == PA_ERR_BAD_SHAPE
     assert _decode(L, c, Hq=7) == PA_ERR_BAD_SHAPE  # not a multiple of Hkv
@@ -182,6 +186,7 @@ def test_append_rejections(L):
     assert _append(L, c, sdt=PA_F32) == PA_ERR_UNSUPPORTED
     assert _append(L, _cache(kv=PA_F32), sdt=PA_BF16) == PA_ERR_UNSUPPORTED
     assert _append(L, _cache(kv=PA_I8), sdt=PA_F32) == PA_ERR_UNSUPPORTED
+    assert _append(L, _cache(kv=PA_I4), sdt=PA_F32) == PA_ERR_UNSUPPORTED
     assert _append(L, c, key=A16[10] + 4) == PA_ERR_MISALIGNED
     assert _append(L, c, slots=A16[12] + 1) == PA_ERR_MISALIGNED
     assert _append(L, c, T=0, key=None, value=None, slots=None) == PA_OK

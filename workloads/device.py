@@ -35,8 +35,13 @@ def src_dtype(kv_dtype: str) -> str:
 
 
 def fill_poison(c: pa.KVCache) -> None:
-    """Fill every pool element with poison (NaN; int8: code -128 with NaN scales)."""
-    if c.kv_dtype == "f32":
+    """Fill every pool element with poison (NaN; int8 / int4: code -128 / -8 with NaN scales)."""
+    if c.kv_dtype == "i4":
+        c.k_cache.fill_(0x88)
+        c.v_cache.fill_(0x88)
+        c.k_scale.fill_(float("nan"))
+        c.v_scale.fill_(float("nan"))
+    elif c.kv_dtype == "f32":
         c.k_cache.fill_(float("nan"))
         c.v_cache.fill_(float("nan"))
     elif c.kv_dtype == "bf16":

@@ -79,7 +79,7 @@ class WorkloadSpec:
     Hkv: int
     D: int
     bs: int
-    kv_dtype: str  # "f32" | "bf16" | "i8"
+    kv_dtype: str  # "f32" | "bf16" | "i8" | "i4"
     q_dtype: str  # "f32" | "bf16"
     scale: float
     max_len: int  # table width = ceil(max_len / bs)
