@@ -49,6 +49,10 @@ constexpr int kInt4 = 2;
 template <int KV>
 constexpr bool kQuant = KV != kBf16;  // codes + fp16 scales per (token, kv head)
 
+// Growth of a row's running maximum (log2 units) that the online softmax
+// absorbs without rescaling its accumulators (probabilities stay < 2^8).
+constexpr float kLazyLog2 = 8.f;
+
 // One K/V storage vector: 16 bytes (8 bf16 or 16 int8 values), or 8 bytes
 // of 16 int4 codes.  int4 keeps the int8 lane mapping with half the bytes.
 template <int KV>
@@ -255,11 +259,18 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   const float m_new = fmaxf(st.m_run, mloc);
-  // a causal query row may see no position of a chunk and nothing before it:
-  // then m_new is -inf and the exponentials below must give 0, not NaN
-  const float m_ref = (CAUSAL && m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m_run - m_ref);
-  st.m_run = m_new;
+  // The exponentials are taken against a reference (st.m_run) that moves only
+  // when a chunk's maximum passes it by more than kLazyLog2, so every
+  // probability stays below 2^kLazyLog2; only then are the accumulators
+  // rescaled, and a wavefront whose rows all keep their reference skips the
+  // rescale.  The result, acc / l, does not depend on the reference.
+  const bool move = m_new > st.m_run + kLazyLog2;  // always, from -inf, once a position is seen
+  const float ref = move ? m_new : st.m_run;
+  // a causal query row may have seen no position yet: its reference is -inf
+  // and the exponentials below must give 0, not NaN
+  const float m_ref = (CAUSAL && ref == -INFINITY) ? 0.f : ref;
+  const float alpha = move ? fast_exp2(st.m_run - m_new) : 1.f;
+  st.m_run = ref;
   float psum = 0.f;
 #pragma unroll
   for (int q = 0; q < T::NQ; ++q) {
@@ -279,8 +290,10 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
     }
   }
   st.l_run = st.l_run * alpha + psum;
+  if (__any(move)) {
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) st.acc[n] *= alpha;
+    for (int n = 0; n < T::ND; ++n) st.acc[n] *= alpha;
+  }
 }
 
 // O^T += V^T P^T, P split into bf16 hi + lo parts.
