@@ -195,14 +195,50 @@ struct Probs {
 template <int KV, int D>
 struct QOp {
   bf16x8 q[Tile<KV, D>::NS];  // B operand of the QK product
+  float bias;                 // int4: 136 * sum of the head's query, removed from its scores
 };
 
 template <int KV, int D>
 struct State {
   f32x4 acc[Tile<KV, D>::ND];  // O^T[16n + 4j + i][head m]
-  float m_run;                 // running max of log2-domain scores (head m)
+  float m_run;                 // reference of the log2-domain exponentials (head m)
   float l_run;                 // this lane's share of the running sum
+  float vsum;                  // int4: this lane's share of sum(p) fed to PV (same reference as acc)
 };
+
+// int4 caches: the K fragments carry 136 + code in even-first element order;
+// give each query k-step the same order and keep 136 * sum(q) of the lane's
+// head, which the scores lose again (the wavefront's lanes j of one head each
+// hold a quarter of its channels).
+template <int KV, int D>
+__device__ __forceinline__ void prepare_qop(QOp<KV, D> &qop) {
+  qop.bias = 0.f;
+  if constexpr (KV == kInt4) {
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < Tile<KV, D>::NS; ++s) {
+      qop.q[s] = __builtin_shufflevector(qop.q[s], qop.q[s], 0, 2, 4, 6, 1, 3, 5, 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += static_cast<float>(qop.q[s][e]);
+    }
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    qop.bias = kInt4Bias * sum;
+  }
+}
+
+// int4 caches: remove 136 * sum(p) from every output of the lane's head (the
+// V fragments carried 136 + code).
+template <int KV, int D>
+__device__ __forceinline__ void finish_state(State<KV, D> &st) {
+  if constexpr (KV == kInt4) {
+    float vs = st.vsum + __shfl_xor(st.vsum, 16);
+    vs = vs + __shfl_xor(vs, 32);
+    const float c = kInt4Bias * vs;
+#pragma unroll
+    for (int n = 0; n < Tile<KV, D>::ND; ++n) st.acc[n] -= c;
+  }
+}
 
 // Scores of one chunk: S^T = K Q^T (row group q holds tokens TPL*j + 4q + i).
 template <int KV, int D>
@@ -219,7 +255,7 @@ __device__ __forceinline__ void qk(Scores<KV, D> &S, const KBuf<KV, D> &kb, cons
         a = (s & 1) ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
       } else if constexpr (KV == kInt4) {
         const u32x2 w = kb.k[q][s >> 1];
-        a = i4x8_to_bf16x8((s & 1) ? w[1] : w[0]);
+        a = i4x8_to_bf16x8_biased((s & 1) ? w[1] : w[0]);
       } else {
         a = __builtin_bit_cast(bf16x8, kb.k[q][s]);
       }
@@ -236,7 +272,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return half_bits_to_float
 // reach t1.
 template <int KV, int D, bool TAIL, bool CAUSAL = false>
 __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, const VBuf<KV, D> &vb, Probs<KV, D> &P,
-                                        int tok0, int t1, float scale_log2) {
+                                        int tok0, int t1, float scale_log2, float sbias) {
   using T = Tile<KV, D>;
   float mloc = -INFINITY;
 #pragma unroll
@@ -247,7 +283,8 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
       float sv;
       if constexpr (kQuant<KV>) {
         const uint32_t kw = vb.ks[e >> 3][(e >> 1) & 3];
-        sv = S.s[q][i] * (scale_log2 * ((e & 1) ? half_hi(kw) : half_lo(kw)));
+        const float raw = KV == kInt4 ? S.s[q][i] - sbias : S.s[q][i];
+        sv = raw * (scale_log2 * ((e & 1) ? half_hi(kw) : half_lo(kw)));
       } else {
         sv = S.s[q][i] * scale_log2;
       }
@@ -290,6 +327,7 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
     }
   }
   st.l_run = st.l_run * alpha + psum;
+  if constexpr (KV == kInt4) st.vsum *= alpha;
   if (__any(move)) {
 #pragma unroll
     for (int n = 0; n < T::ND; ++n) st.acc[n] *= alpha;
@@ -317,10 +355,13 @@ __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, con
     bf16x8 phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = P.p[8 * r + e];
+      // int4 V fragments hold their tokens even-first: P follows
+      const float f = P.p[8 * r + (KV == kInt4 ? kEvenFirst[e] : e)];
       const __bf16 h = static_cast<__bf16>(f);
+      const __bf16 lo = static_cast<__bf16>(f - static_cast<float>(h));
       phi[e] = h;
-      plo[e] = static_cast<__bf16>(f - static_cast<float>(h));
+      plo[e] = lo;
+      if constexpr (KV == kInt4) st.vsum += static_cast<float>(h) + static_cast<float>(lo);
     }
 #pragma unroll
     for (int n = 0; n < T::ND; ++n) {
@@ -330,7 +371,7 @@ __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, con
         a = r ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
       } else if constexpr (KV == kInt4) {
         const u32x2 w = vb.v[n];
-        a = i4x8_to_bf16x8(r ? w[1] : w[0]);
+        a = i4x8_to_bf16x8_biased(r ? w[1] : w[0]);
       } else {
         a = __builtin_bit_cast(bf16x8, vb.v[n]);
       }
@@ -389,7 +430,7 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
     issue_k<NT>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
-  softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2);
+  softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2, qop.bias);
   pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
@@ -525,12 +566,14 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
       qop.q[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  prepare_qop(qop);
 
   State<KV, D> st;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = -INFINITY;
   st.l_run = 0.f;
+  st.vsum = 0.f;
   __syncthreads();  // first table window staged
 
   // ---- token range in windows of staged block-table entries (usually one) ----
@@ -553,6 +596,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
+  finish_state(st);
   float l = st.l_run + __shfl_xor(st.l_run, 16);
   l = l + __shfl_xor(l, 32);
   if (x.m < rows) {
@@ -634,7 +678,7 @@ __device__ __forceinline__ void consume_wide(State<KV, D> (&st)[RW], KBuf<KV, D>
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     Probs<KV, D> P;
-    softmax<KV, D, TAIL, true>(st[r], S[r], vb, P, cs + T::TPL * x.j, t1r[r], scale_log2);
+    softmax<KV, D, TAIL, true>(st[r], S[r], vb, P, cs + T::TPL * x.j, t1r[r], scale_log2, qop[r].bias);
     pv_update<KV, D, TAIL>(st[r], vb, P, cs + T::TPL * x.j, x.t1);
   }
   if constexpr (REFILL) {
@@ -732,6 +776,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
       if (qvalid) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
       qop[r].q[s] = __builtin_bit_cast(bf16x8, v);
     }
+    prepare_qop(qop[r]);
   }
 
   State<KV, D> st[RW];
@@ -741,6 +786,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
     for (int n = 0; n < T::ND; ++n) st[r].acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     st[r].m_run = -INFINITY;
     st[r].l_run = 0.f;
+    st[r].vsum = 0.f;
   }
   __syncthreads();  // first table window staged
 
@@ -760,6 +806,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   // ---- finish this wavefront's rows from registers ----------------------------
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
+    finish_state(st[r]);
     float l = st[r].l_run + __shfl_xor(st[r].l_run, 16);
     l = l + __shfl_xor(l, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -53,18 +53,30 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Eight 4-bit two's-complement codes (nibble k = element k, low nibble
-// first) -> eight bf16 values, exactly (|code| <= 8 needs 4 significant bits).
-__device__ __forceinline__ bf16x8 i4x8_to_bf16x8(uint32_t w) {
+// Eight 4-bit two's-complement codes (nibble e = element e, low nibble
+// first) -> eight bf16 values 136 + code, in the element order
+// 0, 2, 4, 6, 1, 3, 5, 7.  With the codes in offset binary (code + 8 in
+// 0..15), bf16 0x4300 | (code + 8) is exactly 128 + code + 8: one byte
+// permute under the constant 0x43 per two values, no conversion.  The
+// caller removes the 136 offset and lays the other operand out in the same
+// element order.
+constexpr float kInt4Bias = 136.f;
+
+__device__ __forceinline__ bf16x8 i4x8_to_bf16x8_biased(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;         // offset binary in every nibble
+  const uint32_t lo = t & 0x0f0f0f0fu;         // bytes: elements 0, 2, 4, 6
+  const uint32_t hi = (t >> 4) & 0x0f0f0f0fu;  // bytes: elements 1, 3, 5, 7
+  const uint32_t c = 0x43434343u;
   u32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // sign-extend nibbles 2k and 2k+1 by shifting each to the top of a word
-    const float f0 = static_cast<float>(static_cast<int32_t>(w << (28 - 8 * k)) >> 28);
-    const float f1 = static_cast<float>(static_cast<int32_t>(w << (24 - 8 * k)) >> 28);
-    r[k] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-  }
+  // result byte i takes selector byte i: 0-3 pick the second operand's bytes, 4-7 the first's
+  r[0] = __builtin_amdgcn_perm(c, lo, 0x04010400u);  // elements 0, 2
+  r[1] = __builtin_amdgcn_perm(c, lo, 0x04030402u);  // elements 4, 6
+  r[2] = __builtin_amdgcn_perm(c, hi, 0x04010400u);  // elements 1, 3
+  r[3] = __builtin_amdgcn_perm(c, hi, 0x04030402u);  // elements 5, 7
   return __builtin_bit_cast(bf16x8, r);
 }
+
+// Slot s of an i4x8_to_bf16x8_biased result holds element kEvenFirst[s].
+__device__ constexpr int kEvenFirst[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
 }  // namespace pa
