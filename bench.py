@@ -385,27 +385,41 @@ def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flus
     q, tables, lens = meta(w)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
 
-    def run():
+    P = 512  # KV split: more work-groups than the 128-256 units of a single pass
+    pmax = pa.max_partitions(tables.shape[1], 16, P)
+    po = torch.empty((B, Hq, pmax, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((B, Hq, pmax), dtype=torch.float32, device=dev)
+
+    def single():
         pa.decode(q, cache, tables, lens, w.spec.scale, out)
 
-    for _ in range(warmup):
-        flush()
-        run()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        flush()
-        a.record()
-        run()
-        b.record()
-    torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    def split():
+        pa.decode_split(q, cache, tables, lens, w.spec.scale, P, po, pl)
+        pa.reduce(po, pl, lens, P, out)
+
+    def timed(run):
+        for _ in range(warmup):
+            flush()
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            flush()
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    us, us_split = timed(single), timed(split)
     nbytes = perfmodel.decode_bytes(w.context_lens, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype=kv, q_dtype="bf16",
                                     out_dtype="bf16")
-    del cache, out
+    del cache, out, po, pl
     torch.cuda.empty_cache()
+    frac = lambda t: round(nbytes / t / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)  # noqa: E731
     return {"batch": B, "cached_tokens": L, "q_heads": Hq, "kv_heads": Hkv, "kv_dtype": kv, "us": round(us, 2),
-            "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4)}
+            "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": frac(us),
+            "split_512_plus_merge_us": round(us_split, 2), "split_frac_of_hbm_peak": frac(us_split)}
 
 
 def summarise(case: Case, t: dict, peak: float) -> dict:

@@ -898,7 +898,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // a piece index then maps to its sequence by binary search.  No work-group is
 // spent on a partition past the end of its sequence, and the pieces are of
 // near-equal size, so a static stride balances the work.
-template <int KV, int D, int BS, int NW>
+template <int KV, int D, int BS, int NW, int R = 1>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -951,18 +951,20 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
     }
     const int local = piece - sm.first[lo];
     const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
-    if (n_b > 0) run_unit<KV, D, BS, NW>(p, sm, lo, local / n_b, local % n_b);
+    if (n_b > 0) run_unit<KV, D, BS, NW, false, R>(p, sm, lo, local / n_b, local % n_b);
   }
 }
 
 // Split pass: persistent when the sequences' piece offsets fit in LDS,
 // else one work-group per (unit, partition).
-template <int KV, int D, int BS, int NW>
-hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
+template <int KV, int D, int BS, int NW, int R = 1>
+hipError_t launch_split(const DecodeParams &p_in, hipStream_t s) {
+  DecodeParams p = p_in;
+  p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int rows = p.rows_per_group;
   if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
-    const auto kern = decode_split_persistent_kernel<KV, D, BS, NW>;
+    const auto kern = decode_split_persistent_kernel<KV, D, BS, NW, R>;
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -976,9 +978,17 @@ hipError_t launch_split(const DecodeParams &p, hipStream_t s) {
   }
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_num_partitions;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, 0);
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, R>), dim3(static_cast<uint32_t>(nwg)), dim3(NW * 64),
                      lds, s, p);
   return hipGetLastError();
+}
+
+// Split pieces of MQA-like groups (more than 16 query heads per kv head) take
+// two row groups per unit, as single-token units do.
+template <int KV, int D, int BS, int NW>
+hipError_t launch_split_rows(const DecodeParams &p, hipStream_t s) {
+  if (p.head_groups >= 2) return launch_split<KV, D, BS, NW, 2>(p, s);
+  return launch_split<KV, D, BS, NW, 1>(p, s);
 }
 
 // Single pass: one work-group per unit.  Longest sequences first when the
@@ -1073,11 +1083,11 @@ template <int KV, int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
   const bool causal = p.q_start != nullptr;
   if constexpr (kQuant<KV>) {
-    if (p.partition_size > 0) return launch_split<KV, D, BS, 4>(p, s);
+    if (p.partition_size > 0) return launch_split_rows<KV, D, BS, 4>(p, s);
     if (causal) return launch_rows<KV, D, BS, 4, true>(p, s);
     return launch_rows<KV, D, BS, 4, false>(p, s);
   } else {
-    if (p.partition_size > 0) return launch_split<KV, D, BS, 4>(p, s);
+    if (p.partition_size > 0) return launch_split_rows<KV, D, BS, 4>(p, s);
     if (causal) return launch_rows<KV, D, BS, 8, true>(p, s);
     return launch_rows<KV, D, BS, 8, false>(p, s);
   }
