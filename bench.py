@@ -441,6 +441,8 @@ def summarise(case: Case, t: dict, peak: float) -> dict:
                   "decode_logical": case.decode_bytes_logical, "append": case.append_bytes,
                   "split_scratch_overhead": case.scratch_bytes},
     }
+    traffic = measured_traffic(s.name)
+    d["dominant_traffic_bytes"] = traffic["bytes"] if traffic else None
     return d
 
 
