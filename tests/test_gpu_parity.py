@@ -356,3 +356,59 @@ def test_graph_replays_match_eager(cfg):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
+
+
+def test_graph_replays_multi_query_and_int4():
+    """Captured HIP graphs of a multi-query step (append + pa_decode_multi)
+    and of an int4 step (append with nibble atomics + decode) replay to the
+    eager result every time, with eager work between the replays."""
+    from workloads.device import new_token_batch
+    # int4 step
+    w = make_workload(5, small=True, kv_dtype="i4")
+    s = w.spec
+    say("[graph] int4 step")
+    cache = poisoned_cache(w)
+    gpu_append_tokens(w, cache, include_last=False)
+    kn, vn, sl = new_token_batch(w)
+    q, tables, lens = meta(w)
+    out = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    # multi-query step on a bf16 cache (4 new tokens per sequence, causal)
+    wm = make_custom(B=4, Hq=16, Hkv=4, D=128, bs=16, kv_dtype="bf16", lengths=[40, 90, 17, 300], seed=95)
+    cm = poisoned_cache(wm)
+    gpu_append_tokens(wm, cm)
+    qs_np, qm_np = wm.multi_queries(np.full(4, 4, np.int32))
+    from gpu_util import to_dev_values
+    qm = to_dev_values(qm_np, "bf16")
+    qs = torch.from_numpy(qs_np).to(DEV)
+    _, tm, lm = meta(wm)
+    outm = torch.zeros(qm.shape, dtype=torch.float32, device=DEV)
+
+    def step():
+        pa.reshape_and_cache(kn, vn, sl, cache)
+        pa.decode(q, cache, tables, lens, s.scale, out)
+        pa.decode_multi(qm, qs, 4, cm, tm, lm, wm.spec.scale, outm)
+
+    step()
+    torch.cuda.synchronize()
+    ref, refm = out.clone(), outm.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.fill_(float("nan"))
+        outm.fill_(float("nan"))
+        _decode_gpu(w, cache)  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"int4 replay {i}"
+        assert torch.equal(outm, refm), f"multi replay {i}"
+    # the int4 step writes the same bytes every replay (the nibble atomics are idempotent)
+    oc = oracle.build_cache(w)
+    k, v, ks, vs = download_cache(cache)
+    assert np.array_equal(k, oc.packed_k()) and np.array_equal(v, oc.packed_v())
