@@ -116,26 +116,35 @@ class Case:
         else:
             self.scratch_bytes = 0
 
-    def step(self, ev=None):
-        """One decode step; ``ev`` = list of 4 events recorded between its launches."""
+    def step(self):
+        """One decode step as a serving loop issues it: one call (pa_append_decode),
+        or append + split + merge for the KV-split workload."""
         pa, s = self.pa, self.s
-        if ev:
-            ev[0].record()
+        if self.split:
+            pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
+            pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
+                            self.part_out, self.part_lse)
+            pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
+        else:
+            pa.append_decode(self.kn, self.vn, self.slots, self.q, self.cache, self.tables, self.lens, s.scale,
+                             self.out)
+
+    def step_kernels(self, ev):
+        """The same step as separate calls, ``ev`` = 4 events recorded between them
+        (per-kernel times; the events add gaps, so the step is timed by step())."""
+        pa, s = self.pa, self.s
+        ev[0].record()
         pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
-        if ev:
-            ev[1].record()
+        ev[1].record()
         if self.split:
             pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
                             self.part_out, self.part_lse)
-            if ev:
-                ev[2].record()
+            ev[2].record()
             pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
         else:
             pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, self.out)
-            if ev:
-                ev[2].record()
-        if ev:
-            ev[3].record()
+            ev[2].record()
+        ev[3].record()
 
     def decode_f32(self):
         """The same decode into an fp32 output (parity check of the timed path)."""
@@ -173,21 +182,30 @@ class Flush:
 
 
 def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
+    """The step timed by one event pair around it; then the per-kernel times of
+    the same step issued as separate calls with events between them."""
     torch = case.torch
     for i in range(warmup):
         flush()
         case.step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    se = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for i in range(steps):
+    for a, b in se:
         flush()  # evict L2 and Infinity Cache: the step's K/V reads come from HBM
-        case.step(evs[i])
+        a.record()
+        case.step()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step = [a.elapsed_time(b) for a, b in se]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        flush()
+        case.step_kernels(evs[i])
+    torch.cuda.synchronize()
     ms = lambda a, b: [evs[i][a].elapsed_time(evs[i][b]) for i in range(steps)]  # noqa: E731
-    app, dec, tail, step = ms(0, 1), ms(1, 2), ms(2, 3), ms(0, 3)
+    app, dec, tail = ms(0, 1), ms(1, 2), ms(2, 3)
 
     def stats(v):
         v = sorted(v)

@@ -153,6 +153,29 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
                     void *out, pa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * pa_append_decode -- one decode step in one call: pa_reshape_and_cache of
+ * each sequence's new token, then pa_decode over every sequence.
+ *
+ * Token b of key/value ([num_seqs][num_kv_heads][head_dim], src_dtype as for
+ * pa_reshape_and_cache) goes to slot slot_mapping[b] (< 0 skips it), and
+ * sequence b then attends over its L = context_lens[b] cached tokens, the new
+ * one included (the concatenation of page "字节跳动 AI Infra (2)", KV-cache
+ * question, step-t equations).  The results (cache contents and out) are
+ * those of the two calls, bit for bit.  With a bf16, int8 or int4 cache, at
+ * most 16 query heads per kv head and at most 4 (sequence, kv head) pairs
+ * per compute unit it is one kernel: the work-group of each (sequence, kv
+ * head) writes that head's new row, then reads the cache (the append costs
+ * no launch of its own).  Otherwise it makes the two launches.
+ * Preconditions (device data): those of both calls; the new token of
+ * sequence b is its position L - 1, its slot in a block only b references.
+ */
+pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                           const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                           const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, float scale, void *out, pa_dtype out_dtype,
+                           hipStream_t stream);
+
+/*
  * pa_decode_multi -- paged attention of several new query tokens per
  * sequence, causally masked (chunked prefill in small chunks, page
  * "vLLM框架是怎么做推理加速的", section 3; verification of several draft

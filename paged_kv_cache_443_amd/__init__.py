@@ -23,6 +23,7 @@ __all__ = [
     "KVCache",
     "reshape_and_cache",
     "decode",
+    "append_decode",
     "decode_multi",
     "decode_split",
     "reduce",
@@ -177,6 +178,24 @@ def decode(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, context_
                               block_tables.shape[1], _ptr(context_lens), float(scale), _ptr(out), _DT[out.dtype],
                               _stream(q.device))
     _check("pa_decode", st)
+    return out
+
+
+def append_decode(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, q: torch.Tensor, cache: KVCache,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, out: torch.Tensor) -> torch.Tensor:
+    """One decode step: write each sequence's new token (``key``/``value`` ``[B, Hkv, D]``, slots ``[B]``),
+    then decode every sequence into ``out`` ``[B, Hq, D]``.  One kernel where the library fuses them."""
+    B, Hq, D = _decode_args(q, cache, block_tables, context_lens)
+    src = torch.float32 if cache.kv_dtype == "f32" else torch.bfloat16
+    _need(key, "key", src, (B, cache.num_kv_heads, D))
+    _need(value, "value", src, (B, cache.num_kv_heads, D))
+    _need(slot_mapping, "slot_mapping", torch.int32, (B,))
+    _need(out, "out", (torch.float32, torch.bfloat16), (B, Hq, D))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_append_decode(_ptr(key), _ptr(value), _DT[src], _ptr(slot_mapping), _ptr(q), _DT[q.dtype], B, Hq,
+                                     ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                     float(scale), _ptr(out), _DT[out.dtype], _stream(q.device))
+    _check("pa_append_decode", st)
     return out
 
 

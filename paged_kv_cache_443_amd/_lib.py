@@ -27,6 +27,7 @@ PA_I4 = 3
 EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
+    "pa_append_decode",
     "pa_decode_multi",
     "pa_decode_split",
     "pa_reduce",
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [c_void_p, c_int, c_int32, c_int32, P, c_void_p, c_int32, c_void_p, c_float, c_void_p,
                             c_int, c_void_p]
     L.pa_decode.restype = c_int
+    L.pa_append_decode.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int32, c_int32, P,
+                                   c_void_p, c_int32, c_void_p, c_float, c_void_p, c_int, c_void_p]
+    L.pa_append_decode.restype = c_int
     L.pa_decode_multi.argtypes = [c_void_p, c_int, c_int32, c_int32, c_void_p, c_int32, c_int32, P, c_void_p,
                                   c_int32, c_void_p, c_float, c_void_p, c_int, c_void_p]
     L.pa_decode_multi.restype = c_int

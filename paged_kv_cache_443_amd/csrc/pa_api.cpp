@@ -48,6 +48,24 @@ pa::DecodeParams make_decode_params(const void *q, int32_t num_seqs, int32_t num
   return p;
 }
 
+pa::AppendParams make_append_params(const void *key, const void *value, const int32_t *slot_mapping,
+                                    int32_t num_tokens, const pa_kv_cache *cache) {
+  pa::AppendParams p{};
+  p.key = key;
+  p.value = value;
+  p.slot_mapping = slot_mapping;
+  p.k_cache = cache->k_cache;
+  p.v_cache = cache->v_cache;
+  p.k_scale = static_cast<uint16_t *>(cache->k_scale);
+  p.v_scale = static_cast<uint16_t *>(cache->v_scale);
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.block_size = cache->block_size;
+  p.head_dim = cache->head_dim;
+  p.num_blocks = cache->num_blocks;
+  return p;
+}
+
 // Block-table entries a work-group stages at once: the whole range its unit
 // can touch (the table row, or one partition), at most kMaxTableWindow.
 constexpr int32_t kMaxTableWindow = 1024;
@@ -105,19 +123,7 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_
   pa_status st = pa::check_append(key, value, src_dtype, slot_mapping, num_tokens, cache);
   if (st != PA_OK || num_tokens == 0) return st;
   if (static_cast<int64_t>(num_tokens) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
-  pa::AppendParams p{};
-  p.key = key;
-  p.value = value;
-  p.slot_mapping = slot_mapping;
-  p.k_cache = cache->k_cache;
-  p.v_cache = cache->v_cache;
-  p.k_scale = static_cast<uint16_t *>(cache->k_scale);
-  p.v_scale = static_cast<uint16_t *>(cache->v_scale);
-  p.num_tokens = num_tokens;
-  p.num_kv_heads = cache->num_kv_heads;
-  p.block_size = cache->block_size;
-  p.head_dim = cache->head_dim;
-  p.num_blocks = cache->num_blocks;
+  const pa::AppendParams p = make_append_params(key, value, slot_mapping, num_tokens, cache);
   return from_hip(pa::launch_append(p, cache->kv_dtype, stream));
 }
 
@@ -156,6 +162,47 @@ pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int
   p.part_lse = part_lse;
   p.partition_size = partition_size;
   p.max_num_partitions = max_num_partitions;
+  return launch(p, cache, stream);
+}
+
+pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                           const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                           const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, float scale, void *out, pa_dtype out_dtype,
+                           hipStream_t stream) {
+  pa_status st = pa::check_append(key, value, src_dtype, slot_mapping, num_seqs, cache);
+  if (st != PA_OK) return st;
+  st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                               context_lens, scale);
+  if (st != PA_OK || num_seqs == 0) return st;
+  st = pa::check_out(out, q_dtype, cache->kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  const int32_t group = num_heads / cache->num_kv_heads;
+  // Fused only when there are few (sequence, kv head) units per CU: each
+  // unit's work-group then pays its append's latency once before streaming,
+  // which a separate append kernel would have hidden behind the other units
+  // (measured: 70B-shaped workload, 4 units per CU, step 80.4 -> 76.9 us;
+  // LLaMA-13B-shaped, 10 per CU, 269.5 -> 284.6 us).
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return from_hip(e);
+  const bool few_units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads <= 4 * static_cast<int64_t>(cus);
+  if (cache->kv_dtype == PA_F32 || group > 16 || !few_units) {
+    // no fused kernel (fp32 cache, several work-groups per kv head), or many units per CU: two launches
+    st = pa_reshape_and_cache(key, value, src_dtype, slot_mapping, num_seqs, cache, stream);
+    if (st != PA_OK) return st;
+    return pa_decode(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale,
+                     out, out_dtype, stream);
+  }
+  pa::DecodeParams p =
+      make_decode_params(q, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale);
+  p.append = make_append_params(key, value, slot_mapping, num_seqs, cache);
+  p.out = out;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.partition_size = 0;
+  p.max_num_partitions = 1;
   return launch(p, cache, stream);
 }
 

@@ -36,6 +36,7 @@
 
 #include <algorithm>
 
+#include "pa_append_row.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -477,7 +478,7 @@ __device__ __forceinline__ void stream_chunks(State<KV, D> &st, const Ctx<KV, D,
 // group w % R and takes every (NW / R)-th chunk of that group's tokens, so
 // the R groups walk the same K/V chunks at about the same time and all but
 // the first read of each line come from the cache.
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<KV, D>;
   static_assert(NW % R == 0, "row groups must divide the wavefronts");
@@ -512,6 +513,13 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   {
     const int n_first = min(TW, p.max_blocks_per_seq - lb_first);
     for (int i = threadIdx.x; i < n_first; i += NW * 64) sm.tbl[i] = table[lb_first + i];
+  }
+  // fused append + decode (single pass, one unit per (sequence, kv head)):
+  // wavefront 0 writes the sequence's new row for this kv head; the barrier
+  // below makes it visible before any wavefront reads the cache
+  if constexpr (FUSED) {
+    static_assert(!CAUSAL && R == 1, "the fused append needs one unit per (sequence, kv head)");
+    if (w == 0) append_row<KV + 1, D, BS>(p.append, b, kvh, lane);
   }
   const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
   // a partition past the end of its sequence is left untouched (uniform over
@@ -844,7 +852,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p) {
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -887,7 +895,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<KV, D, BS, NW, CAUSAL, R>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<KV, D, BS, NW, CAUSAL, R, FUSED>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -1003,6 +1011,13 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int64_t nwg = static_cast<int64_t>(p.num_kv_heads) * p.head_groups * p.num_seqs;
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
+  if constexpr (!CAUSAL && R == 1) {
+    if (p.append.slot_mapping != nullptr) {  // fused append + decode
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, 1, true>), dim3(static_cast<uint32_t>(nwg)),
+                         dim3(NW * 64), lds, s, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
                      dim3(NW * 64), lds, s, p);
   return hipGetLastError();

@@ -10,6 +10,22 @@
 
 namespace pa {
 
+// Everything one cache append needs (also carried by a fused append + decode).
+struct AppendParams {
+  const void *key;
+  const void *value;
+  const int32_t *slot_mapping;
+  void *k_cache;
+  void *v_cache;
+  uint16_t *k_scale;
+  uint16_t *v_scale;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t num_blocks;
+};
+
 // Everything one decode launch needs, passed by value to the kernel.
 struct DecodeParams {
   const void *q;              // [B][Hq][D]
@@ -32,6 +48,7 @@ struct DecodeParams {
   const int32_t *q_start;     // causal multi-query: [num_seqs + 1] first query row of each sequence, else null
   int32_t num_queries;        // causal multi-query: rows of q and out
   int32_t max_q_len;          // causal multi-query: bound of any sequence's query tokens
+  AppendParams append;        // fused append + decode: token b of each sequence b (slot_mapping null: none)
   int32_t max_blocks_per_seq;
   int32_t num_blocks;
   int32_t partition_size;     // 0: whole sequence (pa_decode)
@@ -56,20 +73,7 @@ struct ReduceParams {
   int32_t out_bf16;
 };
 
-struct AppendParams {
-  const void *key;
-  const void *value;
-  const int32_t *slot_mapping;
-  void *k_cache;
-  void *v_cache;
-  uint16_t *k_scale;
-  uint16_t *v_scale;
-  int32_t num_tokens;
-  int32_t num_kv_heads;
-  int32_t block_size;
-  int32_t head_dim;
-  int32_t num_blocks;
-};
+
 
 // Whole-block copies from one pool to another of the same layout (the same
 // pool for copy-on-write; a GPU pool and a pinned host pool for a swap).

@@ -1,0 +1,78 @@
+"""pa_append_decode (one decode step in one call) vs pa_reshape_and_cache +
+pa_decode and vs the oracle, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_443_amd as pa
+from gpu_util import DEV, TOL, download_cache, gpu_append_tokens, max_err, meta, poisoned_cache, say
+from workloads import make_custom, make_workload
+from workloads.device import new_token_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _two_ways(w, out_dtype=torch.float32):
+    s = w.spec
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    fused = poisoned_cache(w)
+    gpu_append_tokens(w, fused, include_last=False)
+    apart = poisoned_cache(w)
+    gpu_append_tokens(w, apart, include_last=False)
+    out_f = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
+    out_a = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
+    pa.append_decode(kn, vn, sl, q, fused, tables, lens, s.scale, out_f)
+    pa.reshape_and_cache(kn, vn, sl, apart)
+    pa.decode(q, apart, tables, lens, s.scale, out_a)
+    torch.cuda.synchronize()
+    return fused, apart, out_f, out_a
+
+
+def _same_pools(a: pa.KVCache, b: pa.KVCache) -> bool:
+    ka, va, ksa, vsa = download_cache(a)
+    kb, vb, ksb, vsb = download_cache(b)
+    ok = np.array_equal(ka.view(np.uint8), kb.view(np.uint8)) and np.array_equal(va.view(np.uint8), vb.view(np.uint8))
+    if ksa is not None:
+        ok = ok and np.array_equal(ksa.view(np.uint16), ksb.view(np.uint16))
+        ok = ok and np.array_equal(vsa.view(np.uint16), vsb.view(np.uint16))
+    return ok
+
+
+CASES = [
+    ("cfg2", lambda: make_workload(2, small=True)),
+    ("cfg3 beams", lambda: make_workload(3, small=True)),
+    ("cfg5 int8", lambda: make_workload(5, small=True)),
+    ("cfg5 int4", lambda: make_workload(5, small=True, kv_dtype="i4")),
+    ("mha d64 bs32", lambda: make_custom(B=6, Hq=8, Hkv=8, D=64, bs=32, kv_dtype="bf16",
+                                         lengths=[1, 31, 32, 33, 200, 0], seed=21)),
+    # no fused kernel: fp32 cache, and 32 query heads per kv head (two launches)
+    ("cfg1 f32", lambda: make_workload(1)),
+    ("mqa 32 heads", lambda: make_custom(B=4, Hq=32, Hkv=1, D=128, bs=16, kv_dtype="bf16",
+                                         lengths=[5, 70, 16, 300], seed=22)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_fused_step_equals_two_calls_and_oracle(case):
+    name, make = CASES[case]
+    w = make()
+    say(f"[fused] {name} B={w.B}")
+    fused, apart, out_f, out_a = _two_ways(w)
+    assert torch.equal(out_f, out_a), "the fused step must give the two calls' output bit for bit"
+    assert _same_pools(fused, apart), "and the same cache"
+    want = oracle.decode(w.q, oracle.build_cache(w), w.block_tables, w.context_lens, w.spec.scale)
+    err = max_err(out_f, want)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.spec.kv_dtype]
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_fused_step_full_size_bitwise(cfg):
+    """The benchmark's workloads at full size: fused step = two calls, bit for bit."""
+    w = make_workload(cfg)
+    say(f"[fused full] cfg{cfg} B={w.B} tokens={w.total_tokens()}")
+    fused, apart, out_f, out_a = _two_ways(w, torch.bfloat16)
+    assert torch.equal(out_f.view(torch.int16), out_a.view(torch.int16))
+    assert _same_pools(fused, apart)
