@@ -129,22 +129,17 @@ class Case:
             pa.append_decode(self.kn, self.vn, self.slots, self.q, self.cache, self.tables, self.lens, s.scale,
                              self.out)
 
-    def step_kernels(self, ev):
-        """The same step as separate calls, ``ev`` = 4 events recorded between them
-        (per-kernel times; the events add gaps, so the step is timed by step())."""
+    def kernels(self):
+        """The step's kernels as separate calls, by name (each is timed alone)."""
         pa, s = self.pa, self.s
-        ev[0].record()
-        pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
-        ev[1].record()
+        ks = {"append": lambda: pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)}
         if self.split:
-            pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
-                            self.part_out, self.part_lse)
-            ev[2].record()
-            pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
+            ks["decode_split"] = lambda: pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale,
+                                                         s.partition_size, self.part_out, self.part_lse)
+            ks["reduce"] = lambda: pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
         else:
-            pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, self.out)
-            ev[2].record()
-        ev[3].record()
+            ks["decode"] = lambda: pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, self.out)
+        return ks
 
     def decode_f32(self):
         """The same decode into an fp32 output (parity check of the timed path)."""
@@ -181,41 +176,40 @@ class Flush:
         self.torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
-    """The step timed by one event pair around it; then the per-kernel times of
-    the same step issued as separate calls with events between them."""
-    torch = case.torch
-    for i in range(warmup):
+def _timed(torch, fn, steps: int, warmup: int, flush) -> list:
+    """Durations (ms) of ``fn`` over ``steps`` calls, one event pair around each
+    call, the caches flushed before each."""
+    for _ in range(warmup):
         flush()
-        case.step()
+        fn()
     torch.cuda.synchronize()
     se = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in se:
-        flush()  # evict L2 and Infinity Cache: the step's K/V reads come from HBM
+        flush()  # evict L2 and Infinity Cache: the K/V reads come from HBM
         a.record()
-        case.step()
+        fn()
         b.record()
     torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in se]
+
+
+def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
+    """The step timed by one event pair around it; then each of its kernels
+    timed alone in a loop of its own (events between back-to-back launches
+    would add their own gaps to the kernels' times)."""
+    torch = case.torch
+    t0 = time.perf_counter()
+    step = _timed(torch, case.step, steps, warmup, flush)
     wall = time.perf_counter() - t0
-    step = [a.elapsed_time(b) for a, b in se]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for i in range(steps):
-        flush()
-        case.step_kernels(evs[i])
-    torch.cuda.synchronize()
-    ms = lambda a, b: [evs[i][a].elapsed_time(evs[i][b]) for i in range(steps)]  # noqa: E731
-    app, dec, tail = ms(0, 1), ms(1, 2), ms(2, 3)
 
     def stats(v):
         v = sorted(v)
         return {"mean_us": 1e3 * sum(v) / len(v), "median_us": 1e3 * v[len(v) // 2],
                 "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
 
-    r = {"append": stats(app), "decode_split" if case.split else "decode": stats(dec), "step": stats(step),
-         "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
-    if case.split:
-        r["reduce"] = stats(tail)
+    r = {"step": stats(step), "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
+    for name, fn in case.kernels().items():
+        r[name] = stats(_timed(torch, fn, steps, warmup, flush))
     return r
 
 

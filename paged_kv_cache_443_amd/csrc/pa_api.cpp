@@ -179,18 +179,25 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
   if (st != PA_OK) return st;
   if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
   const int32_t group = num_heads / cache->num_kv_heads;
-  // Fused only when there are few (sequence, kv head) units per CU: each
-  // unit's work-group then pays its append's latency once before streaming,
-  // which a separate append kernel would have hidden behind the other units
-  // (measured: 70B-shaped workload, 4 units per CU, step 80.4 -> 76.9 us;
-  // LLaMA-13B-shaped, 10 per CU, 269.5 -> 284.6 us).
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return from_hip(e);
-  const bool few_units = static_cast<int64_t>(num_seqs) * cache->num_kv_heads <= 4 * static_cast<int64_t>(cus);
-  if (cache->kv_dtype == PA_F32 || group > 16 || !few_units) {
-    // no fused kernel (fp32 cache, several work-groups per kv head), or many units per CU: two launches
+  // One kernel when every kv head has one work-group (at most 16 query heads
+  // per kv head).  bf16 caches always: the units take the new row from the
+  // source and append work-groups at the end of the grid write the cache
+  // (measured: 70B-shaped workload 80.4 -> 73.3 us against two launches,
+  // LLaMA-13B-shaped 272.1 -> 261.4 us).  int8 and int4 caches only with at
+  // most 4 (sequence, kv head) units per CU: there the wavefront that reads
+  // the new row writes it first and waits for the store, a round trip per
+  // unit that a separate append kernel hides when the CUs hold many units
+  // (70B-shaped, 4 per CU: 80.4 -> 76.9 us; LLaMA-13B-shaped, 10 per CU:
+  // 269.5 -> 284.6 us).
+  bool fused = cache->kv_dtype != PA_F32 && group <= 16;
+  if (fused && cache->kv_dtype != PA_BF16) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return from_hip(e);
+    fused = static_cast<int64_t>(num_seqs) * cache->num_kv_heads <= 4 * static_cast<int64_t>(cus);
+  }
+  if (!fused) {
     st = pa_reshape_and_cache(key, value, src_dtype, slot_mapping, num_seqs, cache, stream);
     if (st != PA_OK) return st;
     return pa_decode(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale,

@@ -48,22 +48,43 @@ __device__ __forceinline__ void store_pack(E *ptr, const Pack<E, PER> &v) {
 
 }  // namespace append_row_detail
 
-// Token i, kv head h, on the calling wavefront (lane = its lane id).  Lane l
-// owns channels PER*l .. PER*l + PER - 1, which are adjacent in a K tile (one
-// store per lane) and X elements apart in a V tile.  The source rows are
-// loaded alongside the slot, so the only dependent access is the cache write.
-// The whole wavefront must call it (int8 / int4 reduce over it).
-template <int KIND, int D, int BS>  // KIND: 0 fp32, 1 bf16, 2 int8, 3 int4
-__device__ __forceinline__ void append_row(const AppendParams &p, int i, int h, int lane) {
+// The source rows of one (token, kv head), held by one wavefront: lane l
+// owns channels PER*l .. PER*l + PER - 1 of K and of V.
+template <int KIND, int D>  // KIND: 0 fp32, 1 bf16, 2 int8, 3 int4
+struct AppendRowData {
+  typedef typename std::conditional<KIND == 0, float, uint16_t>::type Src;
+  append_row_detail::Pack<Src, D / 64> k, v;
+  int32_t slot;
+};
+
+// Load token i's K and V rows for kv head h and its slot (independent loads).
+template <int KIND, int D>
+__device__ __forceinline__ AppendRowData<KIND, D> load_append_row(const AppendParams &p, int i, int h, int lane) {
   using namespace append_row_detail;
+  using Src = typename AppendRowData<KIND, D>::Src;
+  constexpr int PER = D / 64;
+  AppendRowData<KIND, D> r;
+  r.slot = p.slot_mapping[i];
+  const size_t src = (static_cast<size_t>(i) * p.num_kv_heads + h) * D + PER * lane;
+  r.k = load_pack<Src, PER>(static_cast<const Src *>(p.key) + src);
+  r.v = load_pack<Src, PER>(static_cast<const Src *>(p.value) + src);
+  return r;
+}
+
+// Write loaded rows into their slot of kv head h.  Lane l's channels are
+// adjacent in a K tile (one store per lane) and X elements apart in a V tile.
+// The whole wavefront must call it (int8 / int4 reduce over it).
+template <int KIND, int D, int BS>
+__device__ __forceinline__ void store_append_row(const AppendParams &p, const AppendRowData<KIND, D> &r, int h,
+                                                 int lane) {
+  using namespace append_row_detail;
+  using Src = typename AppendRowData<KIND, D>::Src;
   constexpr int PER = D / 64;
   constexpr int X = KIND == 0 ? 4 : (KIND == 1 ? 8 : 16);  // elements per storage vector
-  typedef typename std::conditional<KIND == 0, float, uint16_t>::type Src;
   const int d0 = PER * lane;
-  const int32_t slot = p.slot_mapping[i];
-  const size_t src = (static_cast<size_t>(i) * p.num_kv_heads + h) * D + d0;
-  const Pack<Src, PER> kk = load_pack<Src, PER>(static_cast<const Src *>(p.key) + src);
-  const Pack<Src, PER> vv = load_pack<Src, PER>(static_cast<const Src *>(p.value) + src);
+  const int32_t slot = r.slot;
+  const Pack<Src, PER> &kk = r.k;
+  const Pack<Src, PER> &vv = r.v;
   if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(p.num_blocks) * BS) return;
   const int pb = slot / BS;
   const int o = slot % BS;
@@ -138,6 +159,14 @@ __device__ __forceinline__ void append_row(const AppendParams &p, int i, int h, 
       }
     }
   }
+}
+
+// Token i, kv head h, on the calling wavefront (lane = its lane id): the
+// rows and the slot are loaded together, so the only dependent access is the
+// cache write.  The whole wavefront must call it.
+template <int KIND, int D, int BS>
+__device__ __forceinline__ void append_row(const AppendParams &p, int i, int h, int lane) {
+  store_append_row<KIND, D, BS>(p, load_append_row<KIND, D>(p, i, h, lane), h, lane);
 }
 
 }  // namespace pa

@@ -119,6 +119,11 @@ struct Ctx {
   int32_t t1_row;   // causal multi-query: this lane's query row sees positions < t1_row
   int32_t t1_min;   // causal multi-query: the smallest t1_row of the unit
   int32_t m, j;
+  // fused append (bf16 caches): position whose K and V come from the new
+  // row rather than the cache (-1: none), and that row as this lane holds
+  // it: channels 2*lane, 2*lane + 1 (head_dim 128) or channel lane (64)
+  int32_t newpos;
+  uint32_t newk, newv;
 };
 
 // K/V tile loads.  Tiles are read once per step and streamed past the caches
@@ -183,6 +188,62 @@ __device__ __forceinline__ void issue_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x
   const typename KvVec<KV>::T *vp = x.vpool + (vtile * (BS / T::X) + ov / T::X) * D + x.m;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<NT>(vp + 16 * n);
+}
+
+// Channels c, c + 1 (c even) of a row spread over the wavefront as above.
+template <int D>
+__device__ __forceinline__ uint32_t row_pair(uint32_t mine, int c) {
+  if constexpr (D == 128)
+    return __shfl(mine, c >> 1);
+  else
+    return (__shfl(mine, c) & 0xffffu) | (__shfl(mine, c + 1) << 16);
+}
+// Channel c of such a row (16 bits).
+template <int D>
+__device__ __forceinline__ uint32_t row_elem(uint32_t mine, int c) {
+  if constexpr (D == 128)
+    return (__shfl(mine, c >> 1) >> (16 * (c & 1))) & 0xffffu;
+  else
+    return __shfl(mine, c) & 0xffffu;
+}
+
+// bf16 K fragments of chunk cs: the lanes whose token is x.newpos take the
+// new row's channels (the bits the cache row will hold).  Every lane joins
+// the shuffles; the caller makes sure the chunk holds x.newpos (uniform).
+template <int D, int BS>
+__device__ __forceinline__ void patch_new_k(KBuf<kBf16, D> &kb, const Ctx<kBf16, D, BS> &x, int cs) {
+  using T = Tile<kBf16, D>;
+#pragma unroll
+  for (int s = 0; s < T::NKL; ++s) {
+    const int c0 = T::X * (4 * s + x.j);  // this lane's vector: channels c0 .. c0 + 7
+    u32x4 row;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) row[w] = row_pair<D>(x.newk, c0 + 2 * w);
+#pragma unroll
+    for (int q = 0; q < T::NQ; ++q) {
+      const int t = cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3);
+      if (t == x.newpos) kb.k[q][s] = row;
+    }
+  }
+}
+
+// bf16 V vectors of a lane group starting at tok0: element newpos - tok0 of
+// channel m + 16n takes the new row's value.
+template <int D>
+__device__ __forceinline__ void patch_new_v(VBuf<kBf16, D> &vb, int tok0, int newpos, uint32_t newv, int m) {
+  using T = Tile<kBf16, D>;
+  const int e = newpos - tok0;
+  const bool hit = e >= 0 && e < T::X;
+  const int k = e >> 1;
+  const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+  const int sh = 16 * (e & 1);
+#pragma unroll
+  for (int n = 0; n < T::ND; ++n) {
+    const uint32_t val = row_elem<D>(newv, m + 16 * n) << sh;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (hit && w == k) vb.v[n][w] = (vb.v[n][w] & keep) | val;
+  }
 }
 
 template <int KV, int D>
@@ -336,10 +397,14 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
 }
 
 // O^T += V^T P^T, P split into bf16 hi + lo parts.
-template <int KV, int D, bool TAIL>
+template <int KV, int D, bool TAIL, bool NEWROW = false>
 __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, const Probs<KV, D> &P, int tok0,
-                                          int t1) {
+                                          int t1, int newpos = -1, uint32_t newv = 0, int m = 0) {
   using T = Tile<KV, D>;
+  if constexpr (NEWROW) {
+    static_assert(TAIL && KV == kBf16, "the new row is spliced into a bf16 chunk's tail");
+    patch_new_v<D>(vb, tok0, newpos, newv, m);
+  }
   if constexpr (TAIL && !kQuant<KV>) {
     // V of positions >= t1 may hold NaN: zero it (0 * NaN would poison the sum)
     uint32_t keep[4];
@@ -418,13 +483,21 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true>
+// NEWROW (a bf16 chunk's tail, fused append): when the chunk holds
+// x.newpos, that position's K and V come from the new row (x.newk, x.newv).
+template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true, bool NEWROW = false>
 __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<KV, D> &vb,
                                         const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop, int cs, int cn, Ids idn,
                                         float scale_log2) {
   using T = Tile<KV, D>;
   Scores<KV, D> S;
   Probs<KV, D> P;
+  bool spliced = false;
+  if constexpr (NEWROW) {
+    static_assert(TAIL && !REFILL && KV == kBf16, "the new row is spliced into a bf16 chunk's tail");
+    spliced = x.newpos >= cs && x.newpos < cs + T::CT;  // uniform over the wavefront
+    if (spliced) patch_new_k<D, BS>(kb, x, cs);
+  }
   qk<KV, D>(S, kb, qop);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +505,14 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2, qop.bias);
-  pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  if constexpr (NEWROW) {
+    if (spliced)
+      pv_update<KV, D, TAIL, true>(st, vb, P, cs + T::TPL * x.j, x.t1, x.newpos, x.newv, x.m);
+    else
+      pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  } else {
+    pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  }
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_v<NT>(vb, x, cn, idn);
@@ -442,7 +522,7 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
 
 // A wavefront's n >= 1 chunks c_i = c0 + i * NW * CT with one chunk in flight
 // while the previous one is computed.
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, bool NT = true>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, bool NT = true, bool NEWROW = false>
 __device__ __forceinline__ void stream_chunks(State<KV, D> &st, const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop,
                                                 int c0, int n, float scale_log2) {
   constexpr int STEP = NW * Tile<KV, D>::CT;
@@ -461,7 +541,8 @@ __device__ __forceinline__ void stream_chunks(State<KV, D> &st, const Ctx<KV, D,
       consume<KV, D, BS, false, true, CAUSAL, NT>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), scale_log2);
     cs = cn;
   }
-  consume<KV, D, BS, true, false, CAUSAL, NT>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, scale_log2);  // may reach past t1
+  consume<KV, D, BS, true, false, CAUSAL, NT, NEWROW>(st, kb, vb, x, qop, cs, 0, Ids{0, 0},
+                                                      scale_log2);  // may reach past t1
 }
 
 // One unit of work: (sequence b, kv head x query-head group hx[, partition]).
@@ -515,12 +596,11 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     for (int i = threadIdx.x; i < n_first; i += NW * 64) sm.tbl[i] = table[lb_first + i];
   }
   // fused append + decode (single pass, one unit per (sequence, kv head)):
-  // wavefront 0 writes the sequence's new row for this kv head; the barrier
-  // below makes it visible before any wavefront reads the cache
-  if constexpr (FUSED) {
-    static_assert(!CAUSAL && R == 1, "the fused append needs one unit per (sequence, kv head)");
-    if (w == 0) append_row<KV + 1, D, BS>(p.append, b, kvh, lane);
-  }
+  // the sequence's new row for this kv head is loaded here, alongside the
+  // table window, and written after the barrier below (see there)
+  static_assert(!FUSED || (!CAUSAL && R == 1), "the fused append needs one unit per (sequence, kv head)");
+  AppendRowData<KV + 1, D> arow;
+  if constexpr (FUSED) arow = load_append_row<KV + 1, D>(p.append, b, kvh, lane);
   const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
   // a partition past the end of its sequence is left untouched (uniform over
   // the work-group, and no barrier has been reached)
@@ -551,6 +631,9 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     if (gcount <= 0) x.t1 = t0;  // a row slot past the last query head
   }
   x.nbv = (x.t1 + BS - 1) / BS;
+  x.newpos = -1;
+  x.newk = 0u;
+  x.newv = 0u;
 
   // ---- query operand (B of the QK product): row r0 + m -------------------------
   QOp<KV, D> qop;
@@ -584,6 +667,40 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   st.vsum = 0.f;
   __syncthreads();  // first table window staged
 
+  // Fused append.  The new token is position L - 1, in a block no other
+  // sequence reads, so the only reader of its bytes is the wavefront whose
+  // chunk holds L - 1 (chunk c of a window belongs to wavefront c mod NWT).
+  //  - bf16: every wavefront holds the new row; the one whose last chunk
+  //    holds L - 1 takes that position's K and V from it (the bits the cache
+  //    row will hold) and nothing here writes the cache: the append
+  //    work-groups at the end of the grid do (decode_mfma_kernel).  A
+  //    wavefront's end waits for its stores to complete, a memory round trip
+  //    that a unit here would add to its time.
+  //  - int8 / int4: that wavefront writes the row before it issues any load;
+  //    a wavefront's accesses to one address are performed in issue order, so
+  //    its later loads of those bytes see the new row.
+  if constexpr (FUSED) {
+    if constexpr (KV == kBf16) {
+      if (L > 0 && arow.slot >= 0 && static_cast<int64_t>(arow.slot) < static_cast<int64_t>(p.num_blocks) * BS) {
+        x.newpos = L - 1;
+        x.newk = arow.k.e[0];
+        x.newv = arow.v.e[0];
+        if constexpr (D == 128) {
+          x.newk |= static_cast<uint32_t>(arow.k.e[1]) << 16;
+          x.newv |= static_cast<uint32_t>(arow.v.e[1]) << 16;
+        }
+      }
+    } else {
+      int owner = 0;  // L == 0: nothing reads the row
+      if (L > 0) {
+        const int span = TW * BS;
+        const int ws_last = (L - 1) / span * span;  // single pass: t0 == 0
+        owner = ((L - 1 - ws_last) / T::CT) % NWT;
+      }
+      if (w == owner) store_append_row<KV + 1, D, BS>(p.append, arow, kvh, lane);
+    }
+  }
+
   // ---- token range in windows of staged block-table entries (usually one) ----
   for (int ws = t0; ws < t1u; ws += TW * BS) {
     const int we = min(ws + TW * BS, t1u);
@@ -600,7 +717,9 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int wew = R == 1 ? we : min(we, x.t1);
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
-    if (n > 0) stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1>(st, x, qop, ws + wt * T::CT, n, p.scale_log2);
+    if (n > 0)
+      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1, FUSED && KV == kBf16>(st, x, qop, ws + wt * T::CT, n,
+                                                                          p.scale_log2);
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
@@ -657,6 +776,34 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
         static_cast<float *>(p.out)[row * D + d] = o;
       }
     }
+  }
+}
+
+// Fused append + decode, bf16 caches: the cache writes of the new rows.  The
+// decode units splice each new row in from the source (run_unit), so no unit
+// reads a row these work-groups write and nothing orders them against the
+// units: they are the grid's last work-groups and run in the launch's tail,
+// where CUs free up.  Each wavefront writes up to kAppendRowsPerWave
+// (token, kv head) rows: all its loads first, then the stores.
+constexpr int kAppendRowsPerWave = 4;
+
+template <int KV, int D, int BS, int NW>
+__device__ __forceinline__ void append_rows(const DecodeParams &p, int first_wg, int nwg) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int rows = p.num_seqs * p.num_kv_heads;
+  const int stride = nwg * NW;
+  const int r0 = first_wg * NW + w;
+  AppendRowData<KV + 1, D> rr[kAppendRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kAppendRowsPerWave; ++k) {
+    const int r = r0 + k * stride;
+    if (r < rows) rr[k] = load_append_row<KV + 1, D>(p.append, r / p.num_kv_heads, r % p.num_kv_heads, lane);
+  }
+#pragma unroll
+  for (int k = 0; k < kAppendRowsPerWave; ++k) {
+    const int r = r0 + k * stride;
+    if (r < rows) store_append_row<KV + 1, D, BS>(p.append, rr[k], r % p.num_kv_heads, lane);
   }
 }
 
@@ -754,6 +901,9 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = tbl;
+  x.newpos = -1;  // no fused append on wide units
+  x.newk = 0u;
+  x.newv = 0u;
 
   // this wavefront's rows end at its last group's last row (none: t1 = 0);
   // the unit's at its last wavefront's
@@ -859,6 +1009,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   const int HX = p.num_kv_heads * p.head_groups;
   const int nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int id = blockIdx.x;
+  if constexpr (FUSED && KV == kBf16) {
+    const int units = HX * p.num_seqs;
+    if (id >= units) {  // an append work-group (uniform)
+      append_rows<KV, D, BS, NW>(p, id - units, static_cast<int>(gridDim.x) - units);
+      return;
+    }
+  }
   const int part = id / (HX * p.num_seqs);
   const int rest = id % (HX * p.num_seqs);
   int b = rest / HX;
@@ -1013,8 +1170,13 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
   if constexpr (!CAUSAL && R == 1) {
     if (p.append.slot_mapping != nullptr) {  // fused append + decode
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, 1, true>), dim3(static_cast<uint32_t>(nwg)),
-                         dim3(NW * 64), lds, s, p);
+      // bf16: append work-groups after the units, kAppendRowsPerWave rows per wavefront
+      const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
+      const int64_t per_wg = static_cast<int64_t>(NW) * kAppendRowsPerWave;
+      const int64_t extra = KV == kBf16 ? (rows + per_wg - 1) / per_wg : 0;
+      if (nwg + extra > INT32_MAX) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, 1, true>),
+                         dim3(static_cast<uint32_t>(nwg + extra)), dim3(NW * 64), lds, s, p);
       return hipGetLastError();
     }
   }

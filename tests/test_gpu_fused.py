@@ -47,6 +47,16 @@ CASES = [
     ("cfg5 int4", lambda: make_workload(5, small=True, kv_dtype="i4")),
     ("mha d64 bs32", lambda: make_custom(B=6, Hq=8, Hkv=8, D=64, bs=32, kv_dtype="bf16",
                                          lengths=[1, 31, 32, 33, 200, 0], seed=21)),
+    # the last chunk's wavefront writes the new row: a second table window
+    # (more than 1024 blocks), blocks spanning two chunks (bs 64), int8 at bs 32
+    ("gqa two windows", lambda: make_custom(B=3, Hq=8, Hkv=2, D=128, bs=16, kv_dtype="bf16",
+                                            lengths=[16400, 16384, 33], seed=23)),
+    ("gqa bs64", lambda: make_custom(B=5, Hq=16, Hkv=2, D=128, bs=64, kv_dtype="bf16",
+                                     lengths=[64, 65, 130, 1, 0], seed=24)),
+    ("int8 d64 bs32", lambda: make_custom(B=4, Hq=8, Hkv=2, D=64, bs=32, kv_dtype="i8",
+                                          lengths=[32, 33, 97, 2], seed=25)),
+    ("int4 bs64", lambda: make_custom(B=4, Hq=8, Hkv=2, D=128, bs=64, kv_dtype="i4",
+                                      lengths=[64, 129, 3, 700], seed=26)),
     # no fused kernel: fp32 cache, and 32 query heads per kv head (two launches)
     ("cfg1 f32", lambda: make_workload(1)),
     ("mqa 32 heads", lambda: make_custom(B=4, Hq=32, Hkv=1, D=128, bs=16, kv_dtype="bf16",
