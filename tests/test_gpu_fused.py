@@ -86,3 +86,40 @@ def test_fused_step_full_size_bitwise(cfg):
     fused, apart, out_f, out_a = _two_ways(w, torch.bfloat16)
     assert torch.equal(out_f.view(torch.int16), out_a.view(torch.int16))
     assert _same_pools(fused, apart)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_fused_step_with_skipped_appends(kv):
+    """Sequences whose new token is not appended (slot -1, or past the pool)
+    read position L - 1 from the cache, as pa_decode does after a skipped
+    append: their key/value rows must not reach the output."""
+    w = make_custom(B=6, Hq=16, Hkv=2, D=128, bs=16, kv_dtype=kv, lengths=[40, 17, 300, 1, 64, 129], seed=27)
+    s = w.spec
+    say(f"[fused skipped] {kv} B={w.B}")
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    sl = sl.clone()
+    sl[1] = -1
+    sl[3] = w.num_blocks * s.bs + 5  # past the pool: the append skips it
+    sl[4] = -1
+    # rows that would change the output if they were used
+    kn = kn * 50
+    vn = vn * 50
+    fused = poisoned_cache(w)
+    gpu_append_tokens(w, fused, include_last=True)
+    apart = poisoned_cache(w)
+    gpu_append_tokens(w, apart, include_last=True)
+    out_f = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    out_a = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    pa.append_decode(kn, vn, sl, q, fused, tables, lens, s.scale, out_f)
+    pa.reshape_and_cache(kn, vn, sl, apart)
+    pa.decode(q, apart, tables, lens, s.scale, out_a)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_a)
+    assert _same_pools(fused, apart)
+    # the skipped sequences still see their original last token
+    want = oracle.decode(w.q, oracle.build_cache(w), w.block_tables, w.context_lens, s.scale)
+    skipped = [1, 3, 4]
+    err = float(np.max(np.abs(out_f[skipped].cpu().numpy().astype(np.float64) - want[skipped])))
+    say(f"  skipped sequences: max abs err {err:.3e}")
+    assert err <= TOL[kv]
