@@ -180,17 +180,16 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
   if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
   const int32_t group = num_heads / cache->num_kv_heads;
   // One kernel when every kv head has one work-group (at most 16 query heads
-  // per kv head).  bf16 caches always: the units take the new row from the
-  // source and append work-groups at the end of the grid write the cache
-  // (measured: 70B-shaped workload 80.4 -> 73.3 us against two launches,
-  // LLaMA-13B-shaped 272.1 -> 261.4 us).  int8 and int4 caches only with at
-  // most 4 (sequence, kv head) units per CU: there the wavefront that reads
-  // the new row writes it first and waits for the store, a round trip per
-  // unit that a separate append kernel hides when the CUs hold many units
-  // (70B-shaped, 4 per CU: 80.4 -> 76.9 us; LLaMA-13B-shaped, 10 per CU:
-  // 269.5 -> 284.6 us).
+  // per kv head).  bf16 and int8 caches always: the units take the new row
+  // from the source (int8: quantised in the kernel exactly as the append
+  // does) and append work-groups at the end of the grid write the cache
+  // (measured against two launches: 70B-shaped workload 80.4 -> 73.3 us,
+  // LLaMA-13B-shaped 272.1 -> 261.4 us).  int4 caches only with at most 4
+  // (sequence, kv head) units per CU: there the wavefront that reads the new
+  // row writes it first and waits for the store, a round trip per unit that a
+  // separate append kernel hides when the CUs hold many units.
   bool fused = cache->kv_dtype != PA_F32 && group <= 16;
-  if (fused && cache->kv_dtype != PA_BF16) {
+  if (fused && cache->kv_dtype == PA_I4) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

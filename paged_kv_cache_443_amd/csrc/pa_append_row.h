@@ -71,6 +71,49 @@ __device__ __forceinline__ AppendRowData<KIND, D> load_append_row(const AppendPa
   return r;
 }
 
+// Symmetric quantisation of a loaded row (int8: KIND 2, qmax 127; int4:
+// KIND 3, qmax 7): per row, the fp16 scale fp16_rne(fp32(max|x| / qmax)) and
+// codes rint_even(fp32(x / scale)) clamped to [-qmax, qmax], all 0 when the
+// scale is 0.  Lane l gets the codes of its channels.  The whole wavefront
+// must call it (the maximum is taken over the wavefront).
+template <int PER>
+struct QuantRow {
+  append_row_detail::Pack<int8_t, PER> k, v;
+  uint16_t sk, sv;
+};
+
+template <int KIND, int D>
+__device__ __forceinline__ QuantRow<D / 64> quantize_row(const AppendRowData<KIND, D> &r) {
+  using namespace append_row_detail;
+  constexpr int PER = D / 64;
+  constexpr float kQmax = KIND == 2 ? 127.0f : 7.0f;
+  QuantRow<PER> out;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const auto &row = which == 0 ? r.k : r.v;
+    float xv[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      xv[k] = bf16_bits_to_float(row.e[k]);
+      amax = fmaxf(amax, fabsf(xv[k]));
+    }
+    amax = wave_max(amax);
+    const uint16_t s16 = float_to_half_bits(amax / kQmax);
+    const float sf = half_bits_to_float(s16);
+    Pack<int8_t, PER> q;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      float qf = 0.f;
+      if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -kQmax), kQmax);
+      q.e[k] = static_cast<int8_t>(static_cast<int>(qf));
+    }
+    (which == 0 ? out.k : out.v) = q;
+    (which == 0 ? out.sk : out.sv) = s16;
+  }
+  return out;
+}
+
 // Write loaded rows into their slot of kv head h.  Lane l's channels are
 // adjacent in a K tile (one store per lane) and X elements apart in a V tile.
 // The whole wavefront must call it (int8 / int4 reduce over it).
@@ -100,29 +143,13 @@ __device__ __forceinline__ void store_append_row(const AppendParams &p, const Ap
 #pragma unroll
       for (int k = 0; k < PER; ++k) vc[v_off<D, BS, X>(tile, o, d0 + k)] = vv.e[k];
     } else {
-      constexpr float kQmax = KIND == 2 ? 127.0f : 7.0f;
       int8_t *kc = static_cast<int8_t *>(p.k_cache);
       int8_t *vc = static_cast<int8_t *>(p.v_cache);
+      const QuantRow<PER> qr = quantize_row<KIND, D>(r);
 #pragma unroll
       for (int which = 0; which < 2; ++which) {
-        const Pack<Src, PER> &row = which == 0 ? kk : vv;
-        float xv[PER];
-        float amax = 0.f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          xv[k] = bf16_bits_to_float(row.e[k]);
-          amax = fmaxf(amax, fabsf(xv[k]));
-        }
-        amax = wave_max(amax);
-        const uint16_t s16 = float_to_half_bits(amax / kQmax);
-        const float sf = half_bits_to_float(s16);
-        Pack<int8_t, PER> q;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          float qf = 0.f;
-          if (sf != 0.f) qf = fminf(fmaxf(rintf(xv[k] / sf), -kQmax), kQmax);
-          q.e[k] = static_cast<int8_t>(static_cast<int>(qf));
-        }
+        const Pack<int8_t, PER> &q = which == 0 ? qr.k : qr.v;
+        const uint16_t s16 = which == 0 ? qr.sk : qr.sv;
         if constexpr (KIND == 2) {
           if (which == 0) {
             store_pack<int8_t, PER>(kc + k_off<D, BS, X>(tile, o, d0), q);

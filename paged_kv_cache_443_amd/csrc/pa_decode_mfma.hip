@@ -119,11 +119,13 @@ struct Ctx {
   int32_t t1_row;   // causal multi-query: this lane's query row sees positions < t1_row
   int32_t t1_min;   // causal multi-query: the smallest t1_row of the unit
   int32_t m, j;
-  // fused append (bf16 caches): position whose K and V come from the new
-  // row rather than the cache (-1: none), and that row as this lane holds
-  // it: channels 2*lane, 2*lane + 1 (head_dim 128) or channel lane (64)
+  // fused append (bf16 and int8 caches): position whose K and V come from
+  // the new row rather than the cache (-1: none), and that row as this lane
+  // holds it: channels 2*lane, 2*lane + 1 (head_dim 128) or channel lane
+  // (64), as bf16 bits or int8 codes (low bytes first); int8: the row's K
+  // scale (low half of news) and V scale (high half), fp16 bits
   int32_t newpos;
-  uint32_t newk, newv;
+  uint32_t newk, newv, news;
 };
 
 // K/V tile loads.  Tiles are read once per step and streamed past the caches
@@ -190,35 +192,59 @@ __device__ __forceinline__ void issue_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x
   for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<NT>(vp + 16 * n);
 }
 
-// Channels c, c + 1 (c even) of a row spread over the wavefront as above.
-template <int D>
-__device__ __forceinline__ uint32_t row_pair(uint32_t mine, int c) {
-  if constexpr (D == 128)
-    return __shfl(mine, c >> 1);
-  else
-    return (__shfl(mine, c) & 0xffffu) | (__shfl(mine, c + 1) << 16);
+// A row spread over the wavefront as in Ctx::newk: the 32 bits holding
+// channels c .. c + 1 (bf16) or c .. c + 3 (int8 codes), c a multiple of
+// that count, and the element of channel c alone.
+template <int KV, int D>
+__device__ __forceinline__ uint32_t row_word(uint32_t mine, int c) {
+  if constexpr (KV == kBf16) {
+    if constexpr (D == 128)
+      return __shfl(mine, c >> 1);
+    else
+      return (__shfl(mine, c) & 0xffffu) | (__shfl(mine, c + 1) << 16);
+  } else {
+    if constexpr (D == 128)
+      return (__shfl(mine, c >> 1) & 0xffffu) | (__shfl(mine, (c >> 1) + 1) << 16);
+    else
+      return (__shfl(mine, c) & 0xffu) | ((__shfl(mine, c + 1) & 0xffu) << 8) |
+             ((__shfl(mine, c + 2) & 0xffu) << 16) | (__shfl(mine, c + 3) << 24);
+  }
 }
-// Channel c of such a row (16 bits).
-template <int D>
+template <int KV, int D>
 __device__ __forceinline__ uint32_t row_elem(uint32_t mine, int c) {
+  constexpr int BITS = KV == kBf16 ? 16 : 8;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
   if constexpr (D == 128)
-    return (__shfl(mine, c >> 1) >> (16 * (c & 1))) & 0xffffu;
+    return (__shfl(mine, c >> 1) >> (BITS * (c & 1))) & MASK;
   else
-    return __shfl(mine, c) & 0xffffu;
+    return __shfl(mine, c) & MASK;
 }
 
-// bf16 K fragments of chunk cs: the lanes whose token is x.newpos take the
-// new row's channels (the bits the cache row will hold).  Every lane joins
-// the shuffles; the caller makes sure the chunk holds x.newpos (uniform).
-template <int D, int BS>
-__device__ __forceinline__ void patch_new_k(KBuf<kBf16, D> &kb, const Ctx<kBf16, D, BS> &x, int cs) {
-  using T = Tile<kBf16, D>;
+// Replace element e (ELEM-bit elements) of a 128-bit vector.
+template <int ELEM>
+__device__ __forceinline__ void set_elem(u32x4 &v, int e, uint32_t val, bool hit) {
+  constexpr int PERW = 32 / ELEM;
+  const int k = e / PERW;
+  const int sh = ELEM * (e % PERW);
+  const uint32_t mask = ((ELEM == 32 ? 0u : (1u << ELEM)) - 1u) << sh;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (hit && w == k) v[w] = (v[w] & ~mask) | ((val << sh) & mask);
+}
+
+// K fragments of chunk cs: the lanes whose token is x.newpos take the new
+// row's channels (the bits the cache row will hold).  Every lane joins the
+// shuffles; the caller makes sure the chunk holds x.newpos (uniform).
+template <int KV, int D, int BS>
+__device__ __forceinline__ void patch_new_k(KBuf<KV, D> &kb, const Ctx<KV, D, BS> &x, int cs) {
+  using T = Tile<KV, D>;
+  constexpr int PERW = KV == kBf16 ? 2 : 4;  // channels per 32-bit word
 #pragma unroll
   for (int s = 0; s < T::NKL; ++s) {
-    const int c0 = T::X * (4 * s + x.j);  // this lane's vector: channels c0 .. c0 + 7
+    const int c0 = T::X * (4 * s + x.j);  // this lane's vector: channels c0 .. c0 + X - 1
     u32x4 row;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) row[w] = row_pair<D>(x.newk, c0 + 2 * w);
+    for (int w = 0; w < 4; ++w) row[w] = row_word<KV, D>(x.newk, c0 + PERW * w);
 #pragma unroll
     for (int q = 0; q < T::NQ; ++q) {
       const int t = cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3);
@@ -227,22 +253,25 @@ __device__ __forceinline__ void patch_new_k(KBuf<kBf16, D> &kb, const Ctx<kBf16,
   }
 }
 
-// bf16 V vectors of a lane group starting at tok0: element newpos - tok0 of
-// channel m + 16n takes the new row's value.
-template <int D>
-__device__ __forceinline__ void patch_new_v(VBuf<kBf16, D> &vb, int tok0, int newpos, uint32_t newv, int m) {
-  using T = Tile<kBf16, D>;
-  const int e = newpos - tok0;
+// The V vectors of a lane group starting at tok0 (element newpos - tok0 of
+// channel m + 16n takes the new row's value) and, int8, the K and V scales
+// of that token.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void patch_new_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x, int tok0) {
+  using T = Tile<KV, D>;
+  const int e = x.newpos - tok0;
   const bool hit = e >= 0 && e < T::X;
-  const int k = e >> 1;
-  const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-  const int sh = 16 * (e & 1);
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n) {
-    const uint32_t val = row_elem<D>(newv, m + 16 * n) << sh;
+  for (int n = 0; n < T::ND; ++n)
+    set_elem<KV == kBf16 ? 16 : 8>(vb.v[n], e, row_elem<KV, D>(x.newv, x.m + 16 * n), hit);
+  if constexpr (KV == kInt8) {
+    // scales of tokens tok0 + 8i .. tok0 + 8i + 7 sit in ks[i] / vs[i]
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (hit && w == k) vb.v[n][w] = (vb.v[n][w] & keep) | val;
+    for (int i = 0; i < 2; ++i) {
+      const bool in = hit && (e >> 3) == i;
+      set_elem<16>(vb.ks[i], e & 7, x.news & 0xffffu, in);
+      set_elem<16>(vb.vs[i], e & 7, x.news >> 16, in);
+    }
   }
 }
 
@@ -397,14 +426,10 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
 }
 
 // O^T += V^T P^T, P split into bf16 hi + lo parts.
-template <int KV, int D, bool TAIL, bool NEWROW = false>
+template <int KV, int D, bool TAIL>
 __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, const Probs<KV, D> &P, int tok0,
-                                          int t1, int newpos = -1, uint32_t newv = 0, int m = 0) {
+                                          int t1) {
   using T = Tile<KV, D>;
-  if constexpr (NEWROW) {
-    static_assert(TAIL && KV == kBf16, "the new row is spliced into a bf16 chunk's tail");
-    patch_new_v<D>(vb, tok0, newpos, newv, m);
-  }
   if constexpr (TAIL && !kQuant<KV>) {
     // V of positions >= t1 may hold NaN: zero it (0 * NaN would poison the sum)
     uint32_t keep[4];
@@ -483,8 +508,8 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-// NEWROW (a bf16 chunk's tail, fused append): when the chunk holds
-// x.newpos, that position's K and V come from the new row (x.newk, x.newv).
+// NEWROW (a chunk's tail, fused append, bf16 or int8): when the chunk holds
+// x.newpos, that position's K and V (and int8 scales) come from the new row.
 template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true, bool NEWROW = false>
 __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<KV, D> &vb,
                                         const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop, int cs, int cn, Ids idn,
@@ -494,25 +519,21 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
   Probs<KV, D> P;
   bool spliced = false;
   if constexpr (NEWROW) {
-    static_assert(TAIL && !REFILL && KV == kBf16, "the new row is spliced into a bf16 chunk's tail");
+    static_assert(TAIL && !REFILL && KV != kInt4, "the new row is spliced into a bf16 or int8 chunk's tail");
     spliced = x.newpos >= cs && x.newpos < cs + T::CT;  // uniform over the wavefront
-    if (spliced) patch_new_k<D, BS>(kb, x, cs);
+    if (spliced) patch_new_k<KV, D, BS>(kb, x, cs);
   }
   qk<KV, D>(S, kb, qop);
+  if constexpr (NEWROW) {
+    if (spliced) patch_new_v<KV, D, BS>(vb, x, cs + T::TPL * x.j);
+  }
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_k<NT>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2, qop.bias);
-  if constexpr (NEWROW) {
-    if (spliced)
-      pv_update<KV, D, TAIL, true>(st, vb, P, cs + T::TPL * x.j, x.t1, x.newpos, x.newv, x.m);
-    else
-      pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
-  } else {
-    pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
-  }
+  pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_v<NT>(vb, x, cn, idn);
@@ -634,6 +655,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   x.newpos = -1;
   x.newk = 0u;
   x.newv = 0u;
+  x.news = 0u;
 
   // ---- query operand (B of the QK product): row r0 + m -------------------------
   QOp<KV, D> qop;
@@ -670,26 +692,38 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   // Fused append.  The new token is position L - 1, in a block no other
   // sequence reads, so the only reader of its bytes is the wavefront whose
   // chunk holds L - 1 (chunk c of a window belongs to wavefront c mod NWT).
-  //  - bf16: every wavefront holds the new row; the one whose last chunk
-  //    holds L - 1 takes that position's K and V from it (the bits the cache
-  //    row will hold) and nothing here writes the cache: the append
-  //    work-groups at the end of the grid do (decode_mfma_kernel).  A
-  //    wavefront's end waits for its stores to complete, a memory round trip
-  //    that a unit here would add to its time.
-  //  - int8 / int4: that wavefront writes the row before it issues any load;
-  //    a wavefront's accesses to one address are performed in issue order, so
+  //  - bf16 and int8: every wavefront holds the new row (int8: quantised as
+  //    the append quantises it); the one whose last chunk holds L - 1 takes
+  //    that position's K and V (and scales) from it, the bits the cache row
+  //    will hold, and nothing here writes the cache: the append work-groups
+  //    at the end of the grid do (decode_mfma_kernel).  A wavefront's end
+  //    waits for its stores to complete, a memory round trip that a unit here
+  //    would add to its time.
+  //  - int4: that wavefront writes the row before it issues any load; a
+  //    wavefront's accesses to one address are performed in issue order, so
   //    its later loads of those bytes see the new row.
   if constexpr (FUSED) {
-    if constexpr (KV == kBf16) {
-      if (L > 0 && arow.slot >= 0 && static_cast<int64_t>(arow.slot) < static_cast<int64_t>(p.num_blocks) * BS) {
-        x.newpos = L - 1;
+    if constexpr (KV != kInt4) {
+      const bool valid =
+          L > 0 && arow.slot >= 0 && static_cast<int64_t>(arow.slot) < static_cast<int64_t>(p.num_blocks) * BS;
+      if constexpr (KV == kBf16) {
         x.newk = arow.k.e[0];
         x.newv = arow.v.e[0];
         if constexpr (D == 128) {
           x.newk |= static_cast<uint32_t>(arow.k.e[1]) << 16;
           x.newv |= static_cast<uint32_t>(arow.v.e[1]) << 16;
         }
+      } else {
+        const QuantRow<D / 64> qr = quantize_row<KV + 1, D>(arow);  // whole wavefront
+        x.newk = static_cast<uint8_t>(qr.k.e[0]);
+        x.newv = static_cast<uint8_t>(qr.v.e[0]);
+        if constexpr (D == 128) {
+          x.newk |= static_cast<uint32_t>(static_cast<uint8_t>(qr.k.e[1])) << 8;
+          x.newv |= static_cast<uint32_t>(static_cast<uint8_t>(qr.v.e[1])) << 8;
+        }
+        x.news = static_cast<uint32_t>(qr.sk) | (static_cast<uint32_t>(qr.sv) << 16);
       }
+      if (valid) x.newpos = L - 1;
     } else {
       int owner = 0;  // L == 0: nothing reads the row
       if (L > 0) {
@@ -718,7 +752,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
     if (n > 0)
-      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1, FUSED && KV == kBf16>(st, x, qop, ws + wt * T::CT, n,
+      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1, FUSED && KV != kInt4>(st, x, qop, ws + wt * T::CT, n,
                                                                           p.scale_log2);
   }
 
@@ -779,7 +813,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
 }
 
-// Fused append + decode, bf16 caches: the cache writes of the new rows.  The
+// Fused append + decode, bf16 and int8 caches: the cache writes of the new rows.  The
 // decode units splice each new row in from the source (run_unit), so no unit
 // reads a row these work-groups write and nothing orders them against the
 // units: they are the grid's last work-groups and run in the launch's tail,
@@ -904,6 +938,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   x.newpos = -1;  // no fused append on wide units
   x.newk = 0u;
   x.newv = 0u;
+  x.news = 0u;
 
   // this wavefront's rows end at its last group's last row (none: t1 = 0);
   // the unit's at its last wavefront's
@@ -1009,7 +1044,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   const int HX = p.num_kv_heads * p.head_groups;
   const int nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int id = blockIdx.x;
-  if constexpr (FUSED && KV == kBf16) {
+  if constexpr (FUSED && KV != kInt4) {
     const int units = HX * p.num_seqs;
     if (id >= units) {  // an append work-group (uniform)
       append_rows<KV, D, BS, NW>(p, id - units, static_cast<int>(gridDim.x) - units);
@@ -1170,10 +1205,10 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
   if constexpr (!CAUSAL && R == 1) {
     if (p.append.slot_mapping != nullptr) {  // fused append + decode
-      // bf16: append work-groups after the units, kAppendRowsPerWave rows per wavefront
+      // bf16 and int8: append work-groups after the units, kAppendRowsPerWave rows per wavefront
       const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
       const int64_t per_wg = static_cast<int64_t>(NW) * kAppendRowsPerWave;
-      const int64_t extra = KV == kBf16 ? (rows + per_wg - 1) / per_wg : 0;
+      const int64_t extra = KV != kInt4 ? (rows + per_wg - 1) / per_wg : 0;
       if (nwg + extra > INT32_MAX) return hipErrorInvalidValue;
       hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, 1, true>),
                          dim3(static_cast<uint32_t>(nwg + extra)), dim3(NW * 64), lds, s, p);
