@@ -508,7 +508,11 @@ def measured_traffic(workload: str):
 # --------------------------------------------------------------------------
 
 
-def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32) -> dict:
+def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32, min_s: float = 10.0) -> dict:
+    """The oracle on one host core over the timed workload's sequences, in
+    order, until ``budget_s`` of work; when the whole batch takes less than
+    ``min_s`` it is passed over again until ``min_s`` (the rate counts every
+    sequence decoded; parity is checked on the first pass)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -520,33 +524,39 @@ def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32) -> dict:
     log("cpu baseline: building the oracle's cache (not timed)")
     oc = oracle.build_cache(w)
     os.sched_setaffinity(0, {allowed[0]})
-    done, secs, toks, errs = [], 0.0, 0, []
+    done, work, secs, toks, errs, passes = [], [], 0.0, 0, [], 0
     try:
         with threadpool_limits(limits=1):
-            for b in range(w.B):
-                sl = [b]
-                t0 = time.perf_counter()
-                want = oracle.decode(w.q[sl], oc, w.block_tables[sl], w.context_lens[sl], s.scale)
-                secs += time.perf_counter() - t0
-                done.append(b)
-                toks += int(w.context_lens[b])
-                errs.append(float(np.max(np.abs(gpu_out_f32[b].astype(np.float64) - want[0]))))
-                if secs >= budget_s:
-                    break
+            while secs < min_s and secs < budget_s:
+                passes += 1
+                for b in range(w.B):
+                    sl = [b]
+                    t0 = time.perf_counter()
+                    want = oracle.decode(w.q[sl], oc, w.block_tables[sl], w.context_lens[sl], s.scale)
+                    secs += time.perf_counter() - t0
+                    work.append(b)
+                    if passes == 1:
+                        done.append(b)
+                        toks += int(w.context_lens[b])
+                        errs.append(float(np.max(np.abs(gpu_out_f32[b].astype(np.float64) - want[0]))))
+                    if secs >= budget_s:
+                        break
     finally:
         os.sched_setaffinity(0, set(allowed))
     kw = dict(Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs, kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
               out_dtype="bf16" if s.q_dtype == "bf16" else "f32")
-    sample_bytes = perfmodel.decode_bytes(w.context_lens[done], **kw)
+    work_bytes = perfmodel.decode_bytes(w.context_lens[work], **kw)  # every sequence decoded, repeats included
+    work_tokens = int(w.context_lens[work].sum())
     return {
-        "value": round(sample_bytes / secs / 1e9, 3),
+        "value": round(work_bytes / secs / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": (f"oracle.decode (numpy fp64) over sequences 0..{done[-1]} of {w.B} ({toks} cached tokens, "
-                   f"{len(done)}/{w.B} of the batch) of the timed workload, one host core of {host_cores}"),
+                   f"{len(done)}/{w.B} of the batch) of the timed workload, {passes} pass(es), "
+                   f"one host core of {host_cores}"),
         "seconds": round(secs, 2),
-        "us_per_step_equiv": round(secs * 1e6 * w.total_tokens() / max(toks, 1), 1),
+        "us_per_step_equiv": round(secs * 1e6 * w.total_tokens() / max(work_tokens, 1), 1),
         "parity_max_abs_err_vs_gpu_fp32_out": max(errs) if errs else None,
     }
 
