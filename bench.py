@@ -118,12 +118,12 @@ class Case:
 
     def step(self):
         """One decode step as a serving loop issues it: one call (pa_append_decode),
-        or append + split + merge for the KV-split workload."""
+        or append + split pass in one call (pa_append_decode_split) and the merge
+        for the KV-split workload."""
         pa, s = self.pa, self.s
         if self.split:
-            pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
-            pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
-                            self.part_out, self.part_lse)
+            pa.append_decode_split(self.kn, self.vn, self.slots, self.q, self.cache, self.tables, self.lens, s.scale,
+                                   s.partition_size, self.part_out, self.part_lse)
             pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
         else:
             pa.append_decode(self.kn, self.vn, self.slots, self.q, self.cache, self.tables, self.lens, s.scale,

@@ -179,6 +179,27 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
                            hipStream_t stream);
 
 /*
+ * pa_append_decode_split -- one KV-split decode step in one call:
+ * pa_reshape_and_cache of each sequence's new token, then pa_decode_split.
+ *
+ * Arguments as for pa_append_decode up to scale, then those of
+ * pa_decode_split.  The results (cache contents, part_out, part_lse) are
+ * those of the two calls, bit for bit; merge them with pa_reduce.  One kernel
+ * for a bf16 or int8 cache with at most 16 query heads per kv head and at
+ * most 4096 sequences: the piece holding position L - 1 takes that position's
+ * K and V (int8: codes and scales, quantised as the append quantises them)
+ * from key/value, and the split pass's work-groups write the new rows after
+ * their last piece; otherwise the two launches.
+ * Preconditions (device data): those of both calls; the new token of
+ * sequence b is its position L - 1, its slot in a block only b references.
+ */
+pa_status pa_append_decode_split(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                                 const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                                 const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, float scale, int32_t partition_size,
+                                 int32_t max_num_partitions, float *part_out, float *part_lse, hipStream_t stream);
+
+/*
  * pa_decode_multi -- paged attention of several new query tokens per
  * sequence, causally masked (chunked prefill in small chunks, page
  * "vLLM框架是怎么做推理加速的", section 3; verification of several draft

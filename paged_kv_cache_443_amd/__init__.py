@@ -24,6 +24,7 @@ __all__ = [
     "reshape_and_cache",
     "decode",
     "append_decode",
+    "append_decode_split",
     "decode_multi",
     "decode_split",
     "reduce",
@@ -197,6 +198,30 @@ def append_decode(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Te
                                      float(scale), _ptr(out), _DT[out.dtype], _stream(q.device))
     _check("pa_append_decode", st)
     return out
+
+
+def append_decode_split(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, q: torch.Tensor,
+                        cache: KVCache, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        partition_size: int, part_out: torch.Tensor, part_lse: torch.Tensor) -> None:
+    """One KV-split decode step: write each sequence's new token, then the split pass into
+    ``part_out`` / ``part_lse`` (merge them with ``reduce``).  One kernel where the library fuses them."""
+    B, Hq, D = _decode_args(q, cache, block_tables, context_lens)
+    src = torch.float32 if cache.kv_dtype == "f32" else torch.bfloat16
+    _need(key, "key", src, (B, cache.num_kv_heads, D))
+    _need(value, "value", src, (B, cache.num_kv_heads, D))
+    _need(slot_mapping, "slot_mapping", torch.int32, (B,))
+    if part_out.dim() != 4:
+        raise ValueError("part_out must be [num_seqs, num_heads, max_num_partitions, head_dim]")
+    Pmax = part_out.shape[2]
+    _need(part_out, "part_out", torch.float32, (B, Hq, Pmax, D))
+    _need(part_lse, "part_lse", torch.float32, (B, Hq, Pmax))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_append_decode_split(_ptr(key), _ptr(value), _DT[src], _ptr(slot_mapping), _ptr(q),
+                                           _DT[q.dtype], B, Hq, ctypes.byref(desc), _ptr(block_tables),
+                                           block_tables.shape[1], _ptr(context_lens), float(scale),
+                                           int(partition_size), Pmax, _ptr(part_out), _ptr(part_lse),
+                                           _stream(q.device))
+    _check("pa_append_decode_split", st)
 
 
 def decode_multi(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, cache: KVCache, block_tables: torch.Tensor,

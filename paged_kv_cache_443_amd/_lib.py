@@ -28,6 +28,7 @@ EXPORTED = (
     "pa_reshape_and_cache",
     "pa_decode",
     "pa_append_decode",
+    "pa_append_decode_split",
     "pa_decode_multi",
     "pa_decode_split",
     "pa_reduce",
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
     L.pa_append_decode.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int32, c_int32, P,
                                    c_void_p, c_int32, c_void_p, c_float, c_void_p, c_int, c_void_p]
     L.pa_append_decode.restype = c_int
+    L.pa_append_decode_split.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int32, c_int32, P,
+                                         c_void_p, c_int32, c_void_p, c_float, c_int32, c_int32, c_void_p, c_void_p,
+                                         c_void_p]
+    L.pa_append_decode_split.restype = c_int
     L.pa_decode_multi.argtypes = [c_void_p, c_int, c_int32, c_int32, c_void_p, c_int32, c_int32, P, c_void_p,
                                   c_int32, c_void_p, c_float, c_void_p, c_int, c_void_p]
     L.pa_decode_multi.restype = c_int

@@ -212,6 +212,44 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
   return launch(p, cache, stream);
 }
 
+pa_status pa_append_decode_split(const void *key, const void *value, pa_dtype src_dtype, const int32_t *slot_mapping,
+                                 const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                                 const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, float scale, int32_t partition_size,
+                                 int32_t max_num_partitions, float *part_out, float *part_lse, hipStream_t stream) {
+  pa_status st = pa::check_append(key, value, src_dtype, slot_mapping, num_seqs, cache);
+  if (st != PA_OK) return st;
+  st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                               context_lens, scale);
+  if (st != PA_OK) return st;
+  st = pa::check_split(partition_size, max_num_partitions, cache->block_size, max_blocks_per_seq, part_out, part_lse);
+  if (st != PA_OK || num_seqs == 0) return st;
+  st = pa::check_out(part_out, q_dtype, cache->kv_dtype, PA_F32);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  // One kernel for bf16 and int8 caches with at most 16 query heads per kv
+  // head and a batch the persistent split pass indexes (pieces splice the
+  // new row; the pass's work-groups write the rows after their last piece);
+  // otherwise the two launches.
+  const int32_t group = num_heads / cache->num_kv_heads;
+  const bool fused = (cache->kv_dtype == PA_BF16 || cache->kv_dtype == PA_I8) && group <= 16 &&
+                     num_seqs <= pa::kMaxFusedSplitSeqs;
+  if (!fused) {
+    st = pa_reshape_and_cache(key, value, src_dtype, slot_mapping, num_seqs, cache, stream);
+    if (st != PA_OK) return st;
+    return pa_decode_split(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens,
+                           scale, partition_size, max_num_partitions, part_out, part_lse, stream);
+  }
+  pa::DecodeParams p =
+      make_decode_params(q, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale);
+  p.append = make_append_params(key, value, slot_mapping, num_seqs, cache);
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.partition_size = partition_size;
+  p.max_num_partitions = max_num_partitions;
+  return launch(p, cache, stream);
+}
+
 pa_status pa_decode_multi(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
                           const int32_t *q_start, int32_t num_queries, int32_t max_q_len, const pa_kv_cache *cache,
                           const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,

@@ -67,6 +67,7 @@ struct KvVec<kInt4> {
 
 // Sequences a persistent split launch can index from LDS (4 bytes each).
 constexpr int kMaxPersistentSeqs = 4096;
+static_assert(kMaxFusedSplitSeqs <= kMaxPersistentSeqs, "fused split batches take the persistent pass");
 // Sequences a single-pass launch ranks by length in every work-group (the
 // ranking costs num_seqs^2 / threads LDS reads per work-group).
 constexpr int kMaxLptSeqs = 512;
@@ -616,9 +617,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int n_first = min(TW, p.max_blocks_per_seq - lb_first);
     for (int i = threadIdx.x; i < n_first; i += NW * 64) sm.tbl[i] = table[lb_first + i];
   }
-  // fused append + decode (single pass, one unit per (sequence, kv head)):
-  // the sequence's new row for this kv head is loaded here, alongside the
-  // table window, and written after the barrier below (see there)
+  // fused append + decode (one unit per (sequence, kv head) or, split, per
+  // (sequence, kv head, partition)): the sequence's new row for this kv head
+  // is loaded here, alongside the table window, and used after the barrier
+  // below (see there)
   static_assert(!FUSED || (!CAUSAL && R == 1), "the fused append needs one unit per (sequence, kv head)");
   AppendRowData<KV + 1, D> arow;
   if constexpr (FUSED) arow = load_append_row<KV + 1, D>(p.append, b, kvh, lane);
@@ -813,12 +815,14 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
 }
 
-// Fused append + decode, bf16 and int8 caches: the cache writes of the new rows.  The
-// decode units splice each new row in from the source (run_unit), so no unit
-// reads a row these work-groups write and nothing orders them against the
-// units: they are the grid's last work-groups and run in the launch's tail,
-// where CUs free up.  Each wavefront writes up to kAppendRowsPerWave
-// (token, kv head) rows: all its loads first, then the stores.
+// Fused append + decode, bf16 and int8 caches: the cache writes of the new
+// rows.  The decode units splice each new row in from the source (run_unit),
+// so no unit reads a row these writes touch and nothing orders them against
+// the units.  Single pass: the grid's last work-groups write them, in the
+// launch's tail where CUs free up; split pass: every persistent work-group
+// writes its share after its last piece.  A wavefront writes
+// kAppendRowsPerWave (token, kv head) rows at a time: all the loads first,
+// then the stores.
 constexpr int kAppendRowsPerWave = 4;
 
 template <int KV, int D, int BS, int NW>
@@ -827,17 +831,18 @@ __device__ __forceinline__ void append_rows(const DecodeParams &p, int first_wg,
   const int w = threadIdx.x >> 6;
   const int rows = p.num_seqs * p.num_kv_heads;
   const int stride = nwg * NW;
-  const int r0 = first_wg * NW + w;
-  AppendRowData<KV + 1, D> rr[kAppendRowsPerWave];
+  for (int r0 = first_wg * NW + w; r0 < rows; r0 += kAppendRowsPerWave * stride) {
+    AppendRowData<KV + 1, D> rr[kAppendRowsPerWave];
 #pragma unroll
-  for (int k = 0; k < kAppendRowsPerWave; ++k) {
-    const int r = r0 + k * stride;
-    if (r < rows) rr[k] = load_append_row<KV + 1, D>(p.append, r / p.num_kv_heads, r % p.num_kv_heads, lane);
-  }
+    for (int k = 0; k < kAppendRowsPerWave; ++k) {
+      const int r = r0 + k * stride;
+      if (r < rows) rr[k] = load_append_row<KV + 1, D>(p.append, r / p.num_kv_heads, r % p.num_kv_heads, lane);
+    }
 #pragma unroll
-  for (int k = 0; k < kAppendRowsPerWave; ++k) {
-    const int r = r0 + k * stride;
-    if (r < rows) store_append_row<KV + 1, D, BS>(p.append, rr[k], r % p.num_kv_heads, lane);
+    for (int k = 0; k < kAppendRowsPerWave; ++k) {
+      const int r = r0 + k * stride;
+      if (r < rows) store_append_row<KV + 1, D, BS>(p.append, rr[k], r % p.num_kv_heads, lane);
+    }
   }
 }
 
@@ -1098,8 +1103,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // a piece index then maps to its sequence by binary search.  No work-group is
 // spent on a partition past the end of its sequence, and the pieces are of
 // near-equal size, so a static stride balances the work.
-template <int KV, int D, int BS, int NW, int R = 1>
+template <int KV, int D, int BS, int NW, int R = 1, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
+  static_assert(!FUSED || (R == 1 && KV != kInt4), "fused split pieces splice a bf16 or int8 row");
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
   const int HX = p.num_kv_heads * p.head_groups;
@@ -1151,8 +1157,9 @@ __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(Decode
     }
     const int local = piece - sm.first[lo];
     const int n_b = (sm.first[lo + 1] - sm.first[lo]) / HX;  // partitions of this sequence (>= 1)
-    if (n_b > 0) run_unit<KV, D, BS, NW, false, R>(p, sm, lo, local / n_b, local % n_b);
+    if (n_b > 0) run_unit<KV, D, BS, NW, false, R, FUSED>(p, sm, lo, local / n_b, local % n_b);
   }
+  if constexpr (FUSED) append_rows<KV, D, BS, NW>(p, blockIdx.x, gridDim.x);
 }
 
 // Split pass: persistent when the sequences' piece offsets fit in LDS,
@@ -1162,9 +1169,17 @@ hipError_t launch_split(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
   p.head_groups = (p.head_groups + R - 1) / R;  // units per kv head
   const int rows = p.rows_per_group;
+  const bool fused = p.append.slot_mapping != nullptr;
+  if constexpr (R != 1 || KV == kInt4) {
+    if (fused) return hipErrorInvalidValue;  // no fused split kernel for these
+  }
+  if (fused && p.num_seqs > kMaxPersistentSeqs) return hipErrorInvalidValue;
   if (p.num_seqs <= kMaxPersistentSeqs) {
     const size_t lds = lds_bytes<D, NW>(p.tbl_window, rows, p.num_seqs + 1);
-    const auto kern = decode_split_persistent_kernel<KV, D, BS, NW, R>;
+    auto kern = decode_split_persistent_kernel<KV, D, BS, NW, R>;
+    if constexpr (R == 1 && KV != kInt4) {
+      if (fused) kern = decode_split_persistent_kernel<KV, D, BS, NW, R, true>;
+    }
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

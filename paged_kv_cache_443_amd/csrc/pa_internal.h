@@ -95,6 +95,10 @@ struct CopyParams {
   size_t tile_bytes;          // one (block, kv head) tile of one pool
 };
 
+// Largest batch the fused append + split pass takes (the persistent split
+// pass indexes its sequences' pieces in LDS).
+constexpr int32_t kMaxFusedSplitSeqs = 4096;
+
 // Launchers (one per kernel family); each returns the launch's hipError_t.
 hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);

@@ -123,3 +123,87 @@ def test_fused_step_with_skipped_appends(kv):
     err = float(np.max(np.abs(out_f[skipped].cpu().numpy().astype(np.float64) - want[skipped])))
     say(f"  skipped sequences: max abs err {err:.3e}")
     assert err <= TOL[kv]
+
+
+SPLIT_CASES = [
+    ("cfg4 long context", lambda: make_workload(4, small=True), None),
+    ("gqa bf16 bs16 P32", lambda: make_custom(B=5, Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16",
+                                              lengths=[1, 31, 32, 33, 700], seed=28), 32),
+    ("gqa int8 bs16 P64", lambda: make_custom(B=4, Hq=8, Hkv=2, D=128, bs=16, kv_dtype="i8",
+                                              lengths=[64, 65, 300, 2], seed=29), 64),
+    ("mha int8 d64 bs32 P32", lambda: make_custom(B=3, Hq=4, Hkv=4, D=64, bs=32, kv_dtype="i8",
+                                                  lengths=[32, 95, 0], seed=30), 32),
+    # not fused: int4 cache, and 32 query heads per kv head (two launches)
+    ("int4 bs16 P32", lambda: make_custom(B=3, Hq=8, Hkv=2, D=128, bs=16, kv_dtype="i4",
+                                          lengths=[40, 3, 200], seed=31), 32),
+    ("mqa 32 heads P32", lambda: make_custom(B=3, Hq=32, Hkv=1, D=128, bs=16, kv_dtype="bf16",
+                                             lengths=[40, 3, 200], seed=32), 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_fused_split_step_equals_two_calls_and_oracle(case):
+    """pa_append_decode_split = pa_reshape_and_cache + pa_decode_split, bit for
+    bit (partials, lse and cache), and the merged result matches the oracle."""
+    name, make, P = SPLIT_CASES[case]
+    w = make()
+    s = w.spec
+    P = P or s.partition_size
+    say(f"[fused split] {name} B={w.B} P={P}")
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    pmax = pa.max_partitions(tables.shape[1], s.bs, P)
+    B, Hq, D = q.shape
+    res = []
+    for fused in (True, False):
+        c = poisoned_cache(w)
+        gpu_append_tokens(w, c, include_last=False)
+        po = torch.full((B, Hq, pmax, D), float("nan"), dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, pmax), float("nan"), dtype=torch.float32, device=DEV)
+        if fused:
+            pa.append_decode_split(kn, vn, sl, q, c, tables, lens, s.scale, P, po, pl)
+        else:
+            pa.reshape_and_cache(kn, vn, sl, c)
+            pa.decode_split(q, c, tables, lens, s.scale, P, po, pl)
+        torch.cuda.synchronize()
+        res.append((c, po, pl))
+    (cf, pof, plf), (ca, poa, pla) = res
+    assert torch.equal(pof.view(torch.int32), poa.view(torch.int32)), "partials must equal the two calls' bit for bit"
+    assert torch.equal(plf.view(torch.int32), pla.view(torch.int32))
+    assert _same_pools(cf, ca)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    pa.reduce(pof, plf, lens, P, out)
+    torch.cuda.synchronize()
+    want = oracle.decode(w.q, oracle.build_cache(w), w.block_tables, w.context_lens, s.scale)
+    err = max_err(out, want)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[s.kv_dtype]
+
+
+def test_fused_split_step_full_size_bitwise():
+    """The long-context workload at full size: fused split step = two calls, bit for bit."""
+    w = make_workload(4)
+    s = w.spec
+    say(f"[fused split full] cfg4 B={w.B} tokens={w.total_tokens()}")
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    pmax = pa.max_partitions(tables.shape[1], s.bs, s.partition_size)
+    B, Hq, D = q.shape
+    res = []
+    for fused in (True, False):
+        c = poisoned_cache(w)
+        gpu_append_tokens(w, c, include_last=False)
+        po = torch.full((B, Hq, pmax, D), float("nan"), dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, pmax), float("nan"), dtype=torch.float32, device=DEV)
+        if fused:
+            pa.append_decode_split(kn, vn, sl, q, c, tables, lens, s.scale, s.partition_size, po, pl)
+        else:
+            pa.reshape_and_cache(kn, vn, sl, c)
+            pa.decode_split(q, c, tables, lens, s.scale, s.partition_size, po, pl)
+        torch.cuda.synchronize()
+        res.append((c, po, pl))
+        del c
+    (cf, pof, plf), (ca, poa, pla) = res
+    assert torch.equal(pof.view(torch.int32), poa.view(torch.int32))
+    assert torch.equal(plf.view(torch.int32), pla.view(torch.int32))
+    assert _same_pools(cf, ca)
