@@ -207,21 +207,29 @@ def test_split_partition_sweep_agrees():
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size_sampled(cfg):
-    """Full-size workload, cache written by the GPU append, decode in the timed
-    launch configuration; sampled sequences checked against the oracle."""
+    """Full-size workload, cache written by the GPU append, then the step the
+    benchmark times (pa_append_decode, or pa_append_decode_split + pa_reduce
+    for the KV-split workload); sampled sequences checked against the oracle."""
+    from workloads.device import new_token_batch
+
     w = make_workload(cfg)
     s = w.spec
     say(f"[full] cfg{cfg} B={w.B} tokens={w.total_tokens()} pool={w.num_blocks}")
     cache = poisoned_cache(w)
     gpu_append_tokens(w, cache, include_last=False)
-    Kn, Vn, sl = w.new_tokens()
-    src = "f32" if s.kv_dtype == "f32" else "bf16"
-    from gpu_util import to_dev_values
-    pa.reshape_and_cache(to_dev_values(Kn, src), to_dev_values(Vn, src), torch.from_numpy(sl).to(DEV), cache)
+    kn, vn, sl = new_token_batch(w)
+    q, tables, lens = meta(w)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     if s.partition_size:
-        _, _, out, _ = _split_gpu(w, cache, s.partition_size)
+        pmax = pa.max_partitions(tables.shape[1], s.bs, s.partition_size)
+        B, Hq, D = q.shape
+        po = torch.full((B, Hq, pmax, D), SENTINEL, dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, pmax), SENTINEL, dtype=torch.float32, device=DEV)
+        pa.append_decode_split(kn, vn, sl, q, cache, tables, lens, s.scale, s.partition_size, po, pl)
+        pa.reduce(po, pl, lens, s.partition_size, out)
     else:
-        out = _decode_gpu(w, cache)
+        pa.append_decode(kn, vn, sl, q, cache, tables, lens, s.scale, out)
+    torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
     rng = np.random.default_rng(cfg)
     picks = sorted(set(rng.choice(w.B, size=min(3, w.B), replace=False).tolist()) | {int(np.argmax(w.context_lens))})
