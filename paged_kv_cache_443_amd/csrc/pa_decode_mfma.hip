@@ -1035,6 +1035,22 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeParams p) {
   run_wide_unit<KV, D, BS, NW, RW>(p, reinterpret_cast<int32_t *>(smem), blockIdx.x / HX, blockIdx.x % HX);
 }
 
+// Several units per (sequence, kv head) (more query-head groups than one
+// unit holds) read the same K/V.  The hardware deals work-groups to the eight
+// XCDs round robin (index mod 8), each XCD with its own L2, so units with
+// neighbouring indices would fetch those lines from HBM once per XCD.  Work-
+// group index id takes unit (pair, g), pair = sequence * kv_heads + kv head,
+// g < HG, laid out in blocks of 8 pairs x HG: the HG units of a pair get
+// indices 8 apart, one XCD, and run side by side, so all but the first read
+// of a line hit that XCD's L2.  A bijection on [0, NP * HG); returns the
+// unit index pair * HG + g.
+__device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
+  const int blk = id / (8 * HG);
+  const int in = id - blk * 8 * HG;
+  const int nb = min(8, NP - blk * 8);  // pairs in this block (the last may hold fewer)
+  return (blk * 8 + in % nb) * HG + in / nb;
+}
+
 // One work-group per unit: (sequence, kv head x query-head group[, partition]).
 // LPT: a single pass over at most kMaxLptSeqs sequences takes the sequences
 // longest first.  The hardware hands out work-groups in index order, so the
@@ -1057,7 +1073,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
   }
   const int part = id / (HX * p.num_seqs);
-  const int rest = id % (HX * p.num_seqs);
+  int rest = id % (HX * p.num_seqs);
+  if (p.partition_size == 0 && p.head_groups > 1)
+    rest = xcd_grouped_unit(rest, p.num_seqs * p.num_kv_heads, p.head_groups);
   int b = rest / HX;
   if (p.lpt) {
     constexpr int NT = NW * 64;
