@@ -381,6 +381,7 @@ def time_multi_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush
 MQA_SHAPES = [
     ("mqa64-bf16", 64, 1, 4096, 128, "bf16"),
     ("mqa64-int8", 64, 1, 4096, 128, "i8"),
+    ("mqa32-bf16", 32, 1, 4096, 128, "bf16"),
 ]
 
 

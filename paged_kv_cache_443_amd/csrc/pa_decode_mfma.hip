@@ -581,7 +581,7 @@ __device__ __forceinline__ void stream_chunks(State<KV, D> &st, const Ctx<KV, D,
 // group w % R and takes every (NW / R)-th chunk of that group's tokens, so
 // the R groups walk the same K/V chunks at about the same time and all but
 // the first read of each line come from the cache.
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false, bool SHARED = false>
 __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, int b, int hx, int part) {
   using T = Tile<KV, D>;
   static_assert(NW % R == 0, "row groups must divide the wavefronts");
@@ -754,8 +754,8 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
     if (n > 0)
-      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1, FUSED && KV != kInt4>(st, x, qop, ws + wt * T::CT, n,
-                                                                          p.scale_log2);
+      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1 && !SHARED, FUSED && KV != kInt4>(st, x, qop, ws + wt * T::CT,
+                                                                                     n, p.scale_log2);
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
@@ -1058,7 +1058,7 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false, bool SHARED = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
     b = len[B];
   }
-  run_unit<KV, D, BS, NW, CAUSAL, R, FUSED>(p, sm, b, rest % HX, min(part, nparts - 1));
+  run_unit<KV, D, BS, NW, CAUSAL, R, FUSED, SHARED>(p, sm, b, rest % HX, min(part, nparts - 1));
 }
 
 // KV-split pass as a persistent kernel: the grid is sized to the work-groups
@@ -1229,7 +1229,7 @@ hipError_t launch_split_rows(const DecodeParams &p, hipStream_t s) {
 // than one work-group, so that another one streams while a work-group ranks
 // (measured: +3 points for four-wave int8 units; with one eight-wave
 // work-group per CU the ranking is dead time and cost 2 points).
-template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1>
+template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool SHARED = false>
 hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   DecodeParams p = p_in;
   p.lpt = (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? 1 : 0;
@@ -1248,7 +1248,7 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, CAUSAL, R>), dim3(static_cast<uint32_t>(nwg)),
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, CAUSAL, R, false, SHARED>), dim3(static_cast<uint32_t>(nwg)),
                      dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
@@ -1308,6 +1308,26 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
     if (wide) return launch_wide<KV, D, BS, NW>(p, s);
   }
   const int most = p.max_q_len > 1 ? NW : 2;
+  // single token (also a multi-query launch bounded to one token, which is
+  // pa_decode bit for bit), several row groups per kv head: two per unit
+  // unless that leaves work-group slots of the GPU empty; then one per unit,
+  // the units of a (sequence, kv head) sharing its lines through the L2
+  // (ordinary loads; they sit on one XCD)
+  if (p.max_q_len <= 1 && rg >= 2) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group,
+                                        (!CAUSAL && NW <= 4 && p.num_seqs <= kMaxLptSeqs) ? p.num_seqs + 1 : 0);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void *>(decode_mfma_kernel<KV, D, BS, NW, CAUSAL, 1, false, true>),
+          NW * 64, lds);
+    if (e != hipSuccess) return e;
+    const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
+    if (pairs * ((rg + 1) / 2) < static_cast<int64_t>(std::max(per_cu, 1)) * cus)
+      return launch_single<KV, D, BS, NW, CAUSAL, 1, true>(p, s);
+  }
   int r = 1;
   while (r < rg && r < most) r *= 2;
   switch (r) {

@@ -154,6 +154,25 @@ def test_edge_lengths_and_groups(kv, bs, D):
         assert max_err(outs, want) <= TOL[kv], ("split", Hq, Hkv)
 
 
+@pytest.mark.parametrize("B,Hq,kv", [(300, 64, "bf16"), (300, 64, "i8"), (600, 64, "i8"), (200, 32, "bf16"),
+                                      (64, 128, "bf16")])
+def test_mqa_batches_both_unit_shapes(B, Hq, kv):
+    """One kv head: units of one or two row groups, chosen from the GPU's
+    work-group slots (large batches take two per unit, small ones one, the
+    units of a sequence sharing its lines); both against the oracle."""
+    rng = np.random.default_rng(B + Hq)
+    lens = rng.integers(0, 300, size=B).tolist()
+    w = make_custom(B=B, Hq=Hq, Hkv=1, D=128, bs=16, kv_dtype=kv, lengths=lens, seed=B * Hq)
+    say(f"[mqa] B={B} Hq={Hq} kv={kv}")
+    oc = oracle.build_cache(w)
+    want = oracle.decode(w.q, oc, w.block_tables, w.context_lens, w.spec.scale)
+    cache = upload_oracle_cache(oc)
+    out = _decode_gpu(w, cache)
+    err = max_err(out, want)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[kv]
+
+
 def test_block_relabel_is_bitwise_invariant():
     w = make_workload(3, small=True)
     say("[relabel] cfg3 small")
