@@ -163,12 +163,12 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
  * question, step-t equations).  The results (cache contents and out) are
  * those of the two calls, bit for bit.  With at most 16 query heads per kv
  * head it is one kernel (the append costs no launch of its own) for a bf16
- * cache, and for an int8 or int4 cache with at most 4 (sequence, kv head)
- * pairs per compute unit; otherwise it makes the two launches.  In the bf16
- * kernel the work-group of each (sequence, kv head) takes position L - 1's
- * K and V from key/value (the bits the cache row receives) and extra
- * work-groups at the end of the grid write the rows; in the int8/int4
- * kernel the work-group writes its head's row before it reads it.
+ * or int8 cache, and for an int4 cache with at most 4 (sequence, kv head)
+ * pairs per compute unit: the work-group of each (sequence, kv head) takes
+ * position L - 1's K and V from key/value (int8/int4: codes and scales,
+ * quantised as the append quantises them; the bits the cache row receives)
+ * and extra work-groups at the end of the grid write the rows.  Otherwise it
+ * makes the two launches.
  * Preconditions (device data): those of both calls; the new token of
  * sequence b is its position L - 1, its slot in a block only b references.
  */

@@ -180,14 +180,14 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
   if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
   const int32_t group = num_heads / cache->num_kv_heads;
   // One kernel when every kv head has one work-group (at most 16 query heads
-  // per kv head).  bf16 and int8 caches always: the units take the new row
-  // from the source (int8: quantised in the kernel exactly as the append
-  // does) and append work-groups at the end of the grid write the cache
+  // per kv head): the units take the new row from the source (int8 / int4:
+  // quantised in the kernel exactly as the append does) and append
+  // work-groups at the end of the grid write the cache.  bf16 and int8 always
   // (measured against two launches: 70B-shaped workload 80.4 -> 73.3 us,
-  // LLaMA-13B-shaped 272.1 -> 261.4 us).  int4 caches only with at most 4
-  // (sequence, kv head) units per CU: there the wavefront that reads the new
-  // row writes it first and waits for the store, a round trip per unit that a
-  // separate append kernel hides when the CUs hold many units.
+  // LLaMA-13B-shaped 272.1 -> 261.4 us, int8 391.7 -> 380.3 us).  int4 only
+  // with at most 4 (sequence, kv head) units per CU: its fused kernel holds
+  // one work-group per CU less (199 VGPRs against 165), which cost the
+  // int8-shaped int4 workload (8 units per CU) 237.8 -> 253.3 us.
   bool fused = cache->kv_dtype != PA_F32 && group <= 16;
   if (fused && cache->kv_dtype == PA_I4) {
     int dev = 0, cus = 0;
@@ -230,7 +230,8 @@ pa_status pa_append_decode_split(const void *key, const void *value, pa_dtype sr
   // One kernel for bf16 and int8 caches with at most 16 query heads per kv
   // head and a batch the persistent split pass indexes (pieces splice the
   // new row; the pass's work-groups write the rows after their last piece);
-  // otherwise the two launches.
+  // otherwise the two launches (int4: the fused pass needs 229 VGPRs, a
+  // work-group per CU less than the plain one).
   const int32_t group = num_heads / cache->num_kv_heads;
   const bool fused = (cache->kv_dtype == PA_BF16 || cache->kv_dtype == PA_I8) && group <= 16 &&
                      num_seqs <= pa::kMaxFusedSplitSeqs;

@@ -194,8 +194,9 @@ __device__ __forceinline__ void issue_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x
 }
 
 // A row spread over the wavefront as in Ctx::newk: the 32 bits holding
-// channels c .. c + 1 (bf16) or c .. c + 3 (int8 codes), c a multiple of
-// that count, and the element of channel c alone.
+// channels c .. c + PERW - 1 as a storage vector holds them (bf16: 2 per
+// word; int8 codes: 4; int4 codes: 8, two per byte, the even channel in the
+// low nibble), c a multiple of PERW, and the element of channel c alone.
 template <int KV, int D>
 __device__ __forceinline__ uint32_t row_word(uint32_t mine, int c) {
   if constexpr (KV == kBf16) {
@@ -203,17 +204,29 @@ __device__ __forceinline__ uint32_t row_word(uint32_t mine, int c) {
       return __shfl(mine, c >> 1);
     else
       return (__shfl(mine, c) & 0xffffu) | (__shfl(mine, c + 1) << 16);
-  } else {
+  } else if constexpr (KV == kInt8) {
     if constexpr (D == 128)
       return (__shfl(mine, c >> 1) & 0xffffu) | (__shfl(mine, (c >> 1) + 1) << 16);
     else
       return (__shfl(mine, c) & 0xffu) | ((__shfl(mine, c + 1) & 0xffu) << 8) |
              ((__shfl(mine, c + 2) & 0xffu) << 16) | (__shfl(mine, c + 3) << 24);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // byte i: channels c + 2i (low nibble), c + 2i + 1
+      uint32_t byte;
+      if constexpr (D == 128)
+        byte = __shfl(mine, (c >> 1) + i) & 0xffu;
+      else
+        byte = (__shfl(mine, c + 2 * i) & 0xfu) | ((__shfl(mine, c + 2 * i + 1) & 0xfu) << 4);
+      w |= byte << (8 * i);
+    }
+    return w;
   }
 }
 template <int KV, int D>
 __device__ __forceinline__ uint32_t row_elem(uint32_t mine, int c) {
-  constexpr int BITS = KV == kBf16 ? 16 : 8;
+  constexpr int BITS = KV == kBf16 ? 16 : (KV == kInt8 ? 8 : 4);
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   if constexpr (D == 128)
     return (__shfl(mine, c >> 1) >> (BITS * (c & 1))) & MASK;
@@ -221,17 +234,23 @@ __device__ __forceinline__ uint32_t row_elem(uint32_t mine, int c) {
     return __shfl(mine, c) & MASK;
 }
 
-// Replace element e (ELEM-bit elements) of a 128-bit vector.
-template <int ELEM>
-__device__ __forceinline__ void set_elem(u32x4 &v, int e, uint32_t val, bool hit) {
+// Replace element e (ELEM-bit elements) of a vector of NW 32-bit words.
+template <int ELEM, int NW, typename Vec>
+__device__ __forceinline__ void set_elem(Vec &v, int e, uint32_t val, bool hit) {
   constexpr int PERW = 32 / ELEM;
   const int k = e / PERW;
   const int sh = ELEM * (e % PERW);
-  const uint32_t mask = ((ELEM == 32 ? 0u : (1u << ELEM)) - 1u) << sh;
+  const uint32_t mask = ((1u << ELEM) - 1u) << sh;
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
+  for (int w = 0; w < NW; ++w)
     if (hit && w == k) v[w] = (v[w] & ~mask) | ((val << sh) & mask);
 }
+
+// 32-bit words in one storage vector, and channels per word.
+template <int KV>
+constexpr int kVecWords = KV == kInt4 ? 2 : 4;
+template <int KV>
+constexpr int kElemBits = KV == kBf16 ? 16 : (KV == kInt8 ? 8 : 4);
 
 // K fragments of chunk cs: the lanes whose token is x.newpos take the new
 // row's channels (the bits the cache row will hold).  Every lane joins the
@@ -239,13 +258,13 @@ __device__ __forceinline__ void set_elem(u32x4 &v, int e, uint32_t val, bool hit
 template <int KV, int D, int BS>
 __device__ __forceinline__ void patch_new_k(KBuf<KV, D> &kb, const Ctx<KV, D, BS> &x, int cs) {
   using T = Tile<KV, D>;
-  constexpr int PERW = KV == kBf16 ? 2 : 4;  // channels per 32-bit word
+  constexpr int PERW = 32 / kElemBits<KV>;  // channels per 32-bit word
 #pragma unroll
   for (int s = 0; s < T::NKL; ++s) {
     const int c0 = T::X * (4 * s + x.j);  // this lane's vector: channels c0 .. c0 + X - 1
-    u32x4 row;
+    typename KvVec<KV>::T row;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) row[w] = row_word<KV, D>(x.newk, c0 + PERW * w);
+    for (int w = 0; w < kVecWords<KV>; ++w) row[w] = row_word<KV, D>(x.newk, c0 + PERW * w);
 #pragma unroll
     for (int q = 0; q < T::NQ; ++q) {
       const int t = cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3);
@@ -255,8 +274,8 @@ __device__ __forceinline__ void patch_new_k(KBuf<KV, D> &kb, const Ctx<KV, D, BS
 }
 
 // The V vectors of a lane group starting at tok0 (element newpos - tok0 of
-// channel m + 16n takes the new row's value) and, int8, the K and V scales
-// of that token.
+// channel m + 16n takes the new row's value) and, int8 / int4, the K and V
+// scales of that token.
 template <int KV, int D, int BS>
 __device__ __forceinline__ void patch_new_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x, int tok0) {
   using T = Tile<KV, D>;
@@ -264,14 +283,14 @@ __device__ __forceinline__ void patch_new_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS
   const bool hit = e >= 0 && e < T::X;
 #pragma unroll
   for (int n = 0; n < T::ND; ++n)
-    set_elem<KV == kBf16 ? 16 : 8>(vb.v[n], e, row_elem<KV, D>(x.newv, x.m + 16 * n), hit);
-  if constexpr (KV == kInt8) {
+    set_elem<kElemBits<KV>, kVecWords<KV>>(vb.v[n], e, row_elem<KV, D>(x.newv, x.m + 16 * n), hit);
+  if constexpr (kQuant<KV>) {
     // scales of tokens tok0 + 8i .. tok0 + 8i + 7 sit in ks[i] / vs[i]
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const bool in = hit && (e >> 3) == i;
-      set_elem<16>(vb.ks[i], e & 7, x.news & 0xffffu, in);
-      set_elem<16>(vb.vs[i], e & 7, x.news >> 16, in);
+      set_elem<16, 4>(vb.ks[i], e & 7, x.news & 0xffffu, in);
+      set_elem<16, 4>(vb.vs[i], e & 7, x.news >> 16, in);
     }
   }
 }
@@ -509,8 +528,8 @@ __device__ __forceinline__ Smem carve(unsigned char *smem, int TW, int rows) {
 // read (K after QK, V after PV), for chunk `cn` with block ids `idn`.
 // (sched_barrier pins the load issue points: left alone, the scheduler sinks
 // them next to their first use and nothing stays in flight.)
-// NEWROW (a chunk's tail, fused append, bf16 or int8): when the chunk holds
-// x.newpos, that position's K and V (and int8 scales) come from the new row.
+// NEWROW (a chunk's tail, fused append): when the chunk holds x.newpos, that
+// position's K and V (and int8 / int4 scales) come from the new row.
 template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL = false, bool NT = true, bool NEWROW = false>
 __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<KV, D> &vb,
                                         const Ctx<KV, D, BS> &x, const QOp<KV, D> &qop, int cs, int cn, Ids idn,
@@ -520,7 +539,7 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
   Probs<KV, D> P;
   bool spliced = false;
   if constexpr (NEWROW) {
-    static_assert(TAIL && !REFILL && KV != kInt4, "the new row is spliced into a bf16 or int8 chunk's tail");
+    static_assert(TAIL && !REFILL, "the new row is spliced into a chunk's tail");
     spliced = x.newpos >= cs && x.newpos < cs + T::CT;  // uniform over the wavefront
     if (spliced) patch_new_k<KV, D, BS>(kb, x, cs);
   }
@@ -693,48 +712,44 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 
   // Fused append.  The new token is position L - 1, in a block no other
   // sequence reads, so the only reader of its bytes is the wavefront whose
-  // chunk holds L - 1 (chunk c of a window belongs to wavefront c mod NWT).
-  //  - bf16 and int8: every wavefront holds the new row (int8: quantised as
-  //    the append quantises it); the one whose last chunk holds L - 1 takes
-  //    that position's K and V (and scales) from it, the bits the cache row
-  //    will hold, and nothing here writes the cache: the append work-groups
-  //    at the end of the grid do (decode_mfma_kernel).  A wavefront's end
-  //    waits for its stores to complete, a memory round trip that a unit here
-  //    would add to its time.
-  //  - int4: that wavefront writes the row before it issues any load; a
-  //    wavefront's accesses to one address are performed in issue order, so
-  //    its later loads of those bytes see the new row.
+  // chunk holds L - 1.  Every wavefront holds the new row (int8 / int4:
+  // quantised as the append quantises it, codes packed as the cache packs
+  // them); the one whose last chunk holds L - 1 takes that position's K and
+  // V (and scales) from it, the bits the cache row will hold, and nothing
+  // here writes the cache: append work-groups do (append_rows).  A
+  // wavefront's end, and any later wait on its memory counter, waits for its
+  // stores to complete, a memory round trip that a unit here would add to
+  // its time.
   if constexpr (FUSED) {
-    if constexpr (KV != kInt4) {
-      const bool valid =
-          L > 0 && arow.slot >= 0 && static_cast<int64_t>(arow.slot) < static_cast<int64_t>(p.num_blocks) * BS;
-      if constexpr (KV == kBf16) {
-        x.newk = arow.k.e[0];
-        x.newv = arow.v.e[0];
-        if constexpr (D == 128) {
-          x.newk |= static_cast<uint32_t>(arow.k.e[1]) << 16;
-          x.newv |= static_cast<uint32_t>(arow.v.e[1]) << 16;
-        }
-      } else {
-        const QuantRow<D / 64> qr = quantize_row<KV + 1, D>(arow);  // whole wavefront
+    const bool valid =
+        L > 0 && arow.slot >= 0 && static_cast<int64_t>(arow.slot) < static_cast<int64_t>(p.num_blocks) * BS;
+    if constexpr (KV == kBf16) {
+      x.newk = arow.k.e[0];
+      x.newv = arow.v.e[0];
+      if constexpr (D == 128) {
+        x.newk |= static_cast<uint32_t>(arow.k.e[1]) << 16;
+        x.newv |= static_cast<uint32_t>(arow.v.e[1]) << 16;
+      }
+    } else {
+      const QuantRow<D / 64> qr = quantize_row<KV + 1, D>(arow);  // whole wavefront
+      if constexpr (KV == kInt8) {
         x.newk = static_cast<uint8_t>(qr.k.e[0]);
         x.newv = static_cast<uint8_t>(qr.v.e[0]);
         if constexpr (D == 128) {
           x.newk |= static_cast<uint32_t>(static_cast<uint8_t>(qr.k.e[1])) << 8;
           x.newv |= static_cast<uint32_t>(static_cast<uint8_t>(qr.v.e[1])) << 8;
         }
-        x.news = static_cast<uint32_t>(qr.sk) | (static_cast<uint32_t>(qr.sv) << 16);
+      } else {  // int4: a nibble per channel, the even channel low
+        x.newk = static_cast<uint32_t>(qr.k.e[0]) & 0xfu;
+        x.newv = static_cast<uint32_t>(qr.v.e[0]) & 0xfu;
+        if constexpr (D == 128) {
+          x.newk |= (static_cast<uint32_t>(qr.k.e[1]) & 0xfu) << 4;
+          x.newv |= (static_cast<uint32_t>(qr.v.e[1]) & 0xfu) << 4;
+        }
       }
-      if (valid) x.newpos = L - 1;
-    } else {
-      int owner = 0;  // L == 0: nothing reads the row
-      if (L > 0) {
-        const int span = TW * BS;
-        const int ws_last = (L - 1) / span * span;  // single pass: t0 == 0
-        owner = ((L - 1 - ws_last) / T::CT) % NWT;
-      }
-      if (w == owner) store_append_row<KV + 1, D, BS>(p.append, arow, kvh, lane);
+      x.news = static_cast<uint32_t>(qr.sk) | (static_cast<uint32_t>(qr.sv) << 16);
     }
+    if (valid) x.newpos = L - 1;
   }
 
   // ---- token range in windows of staged block-table entries (usually one) ----
@@ -754,8 +769,8 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
     const int nch = wew > ws ? (wew - ws + T::CT - 1) / T::CT : 0;
     const int n = wt < nch ? (nch - wt + NWT - 1) / NWT : 0;
     if (n > 0)
-      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1 && !SHARED, FUSED && KV != kInt4>(st, x, qop, ws + wt * T::CT,
-                                                                                     n, p.scale_log2);
+      stream_chunks<KV, D, BS, NWT, CAUSAL, R == 1 && !SHARED, FUSED>(st, x, qop, ws + wt * T::CT, n,
+                                                                      p.scale_log2);
   }
 
   // ---- merge the wavefronts' states -------------------------------------------
@@ -815,8 +830,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
 }
 
-// Fused append + decode, bf16 and int8 caches: the cache writes of the new
-// rows.  The decode units splice each new row in from the source (run_unit),
+// Fused append + decode: the cache writes of the new rows.  The decode units splice each new row in from the source (run_unit),
 // so no unit reads a row these writes touch and nothing orders them against
 // the units.  Single pass: the grid's last work-groups write them, in the
 // launch's tail where CUs free up; split pass: every persistent work-group
@@ -1065,7 +1079,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   const int HX = p.num_kv_heads * p.head_groups;
   const int nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int id = blockIdx.x;
-  if constexpr (FUSED && KV != kInt4) {
+  if constexpr (FUSED) {
     const int units = HX * p.num_seqs;
     if (id >= units) {  // an append work-group (uniform)
       append_rows<KV, D, BS, NW>(p, id - units, static_cast<int>(gridDim.x) - units);
@@ -1123,7 +1137,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 // near-equal size, so a static stride balances the work.
 template <int KV, int D, int BS, int NW, int R = 1, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64) void decode_split_persistent_kernel(DecodeParams p) {
-  static_assert(!FUSED || (R == 1 && KV != kInt4), "fused split pieces splice a bf16 or int8 row");
+  static_assert(!FUSED || (R == 1 && KV != kInt4), "fused split pieces: bf16 or int8, one unit per piece");
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
   const int HX = p.num_kv_heads * p.head_groups;
@@ -1238,10 +1252,10 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
   const size_t lds = lds_bytes<D, NW>(p.tbl_window, p.rows_per_group, p.lpt ? p.num_seqs + 1 : 0);
   if constexpr (!CAUSAL && R == 1) {
     if (p.append.slot_mapping != nullptr) {  // fused append + decode
-      // bf16 and int8: append work-groups after the units, kAppendRowsPerWave rows per wavefront
+      // append work-groups after the units, kAppendRowsPerWave rows per wavefront
       const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
       const int64_t per_wg = static_cast<int64_t>(NW) * kAppendRowsPerWave;
-      const int64_t extra = KV != kInt4 ? (rows + per_wg - 1) / per_wg : 0;
+      const int64_t extra = (rows + per_wg - 1) / per_wg;
       if (nwg + extra > INT32_MAX) return hipErrorInvalidValue;
       hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, NW, false, 1, true>),
                          dim3(static_cast<uint32_t>(nwg + extra)), dim3(NW * 64), lds, s, p);

@@ -78,17 +78,17 @@ def test_fused_step_equals_two_calls_and_oracle(case):
     assert err <= TOL[w.spec.kv_dtype]
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 5, "5-int4"])
 def test_fused_step_full_size_bitwise(cfg):
     """The benchmark's workloads at full size: fused step = two calls, bit for bit."""
-    w = make_workload(cfg)
+    w = make_workload(5, kv_dtype="i4") if cfg == "5-int4" else make_workload(cfg)
     say(f"[fused full] cfg{cfg} B={w.B} tokens={w.total_tokens()}")
     fused, apart, out_f, out_a = _two_ways(w, torch.bfloat16)
     assert torch.equal(out_f.view(torch.int16), out_a.view(torch.int16))
     assert _same_pools(fused, apart)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
 def test_fused_step_with_skipped_appends(kv):
     """Sequences whose new token is not appended (slot -1, or past the pool)
     read position L - 1 from the cache, as pa_decode does after a skipped
