@@ -1,4 +1,4 @@
-// Paged decode attention on the CDNA4 matrix cores (bf16 and int8 KV caches).
+// Paged decode attention on the CDNA4 matrix cores (bf16, int8 and int4 KV caches).
 //
 // What is computed (page "字节跳动 AI Infra (2)", KV-cache question, step-t
 // equations): for each sequence and query head, softmax(scale * q . k_t)
@@ -14,8 +14,8 @@
 //
 // Work decomposition.  One work-group (NW wavefronts) per (kv head, group of
 // <= 16 query heads, sequence[, partition]).  The wavefronts interleave over
-// chunks of CT consecutive tokens (32 for bf16, 64 for int8: 16 KiB of K+V
-// per chunk at head_dim 128), keep one chunk in flight while computing the
+// chunks of CT consecutive tokens (32 for bf16, 64 for int8 and int4: 16 KiB
+// and 8 KiB of K+V per chunk at head_dim 128), keep one chunk in flight while computing the
 // previous one, and merge their softmax states through LDS at the end.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, wave64):
@@ -120,10 +120,11 @@ struct Ctx {
   int32_t t1_row;   // causal multi-query: this lane's query row sees positions < t1_row
   int32_t t1_min;   // causal multi-query: the smallest t1_row of the unit
   int32_t m, j;
-  // fused append (bf16 and int8 caches): position whose K and V come from
-  // the new row rather than the cache (-1: none), and that row as this lane
-  // holds it: channels 2*lane, 2*lane + 1 (head_dim 128) or channel lane
-  // (64), as bf16 bits or int8 codes (low bytes first); int8: the row's K
+  // fused append: position whose K and V come from the new row rather than
+  // the cache (-1: none), and that row as this lane holds it: channels
+  // 2*lane, 2*lane + 1 (head_dim 128) or channel lane (64), as bf16 bits,
+  // int8 codes (a byte each, the lower channel first) or int4 codes (a nibble
+  // each, the lower channel in the low nibble); int8 / int4: the row's K
   // scale (low half of news) and V scale (high half), fp16 bits
   int32_t newpos;
   uint32_t newk, newv, news;
@@ -1072,6 +1073,9 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
 // first the tail is made of the shortest ones.  Every work-group ranks the
 // lengths in LDS (ties by index) and serves the sequence whose rank is its
 // index / (head units); the output is the same for any order.
+// FUSED: the grid's last work-groups write the new rows (append_rows) and the
+// units splice them in.  SHARED: single-row-group units whose siblings read
+// the same K/V (ordinary loads, so the lines stay in the XCD's L2).
 template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false, bool SHARED = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1275,10 +1279,12 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
 // Units with several query tokens are compute-heavy: all groups in one unit
 // (R up to the wavefront count; 512-token chunks ran 2.5x faster than one
 // group per unit).  Single-token units stream: two groups per unit (on one kv
-// head with 32 to 128 query heads, bf16 and int8, two per unit beat one by
-// 1.1-2.0x and four or eight by 1.3-2.4x).  The choice depends on the launch
-// shape only, so a multi-query launch with one token per sequence is the
-// single-token launch.
+// head with 32 to 128 query heads, bf16 and int8, two per unit beat four or
+// eight by 1.3-2.4x), or one per unit with the units of a kv head sharing its
+// lines through their XCD's L2 when two per unit would leave work-group
+// slots empty (launch_rows).  The choice depends on the launch shape only,
+// so a multi-query launch with one token per sequence is the single-token
+// launch.
 // Wide multi-query units: RW row groups per wavefront, NW * RW per unit.
 constexpr int kWideRowGroups = 2;
 
