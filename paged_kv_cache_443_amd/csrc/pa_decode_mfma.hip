@@ -446,8 +446,9 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
   }
 }
 
-// O^T += V^T P^T, P split into bf16 hi + lo parts.
-template <int KV, int D, bool TAIL>
+// O^T += V^T P^T, P split into bf16 hi + lo parts (LO), or P rounded to
+// bf16 once (one product; the wide multi-query units).
+template <int KV, int D, bool TAIL, bool LO = true>
 __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, const Probs<KV, D> &P, int tok0,
                                           int t1) {
   using T = Tile<KV, D>;
@@ -470,10 +471,14 @@ __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, con
       // int4 V fragments hold their tokens even-first: P follows
       const float f = P.p[8 * r + (KV == kInt4 ? kEvenFirst[e] : e)];
       const __bf16 h = static_cast<__bf16>(f);
-      const __bf16 lo = static_cast<__bf16>(f - static_cast<float>(h));
       phi[e] = h;
-      plo[e] = lo;
-      if constexpr (KV == kInt4) st.vsum += static_cast<float>(h) + static_cast<float>(lo);
+      if constexpr (LO) {
+        const __bf16 lo = static_cast<__bf16>(f - static_cast<float>(h));
+        plo[e] = lo;
+        if constexpr (KV == kInt4) st.vsum += static_cast<float>(h) + static_cast<float>(lo);
+      } else if constexpr (KV == kInt4) {
+        st.vsum += static_cast<float>(h);
+      }
     }
 #pragma unroll
     for (int n = 0; n < T::ND; ++n) {
@@ -488,7 +493,7 @@ __device__ __forceinline__ void pv_update(State<KV, D> &st, VBuf<KV, D> &vb, con
         a = __builtin_bit_cast(bf16x8, vb.v[n]);
       }
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[n], 0, 0, 0);
-      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[n], 0, 0, 0);
+      if constexpr (LO) st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[n], 0, 0, 0);
     }
   }
 }
@@ -888,7 +893,7 @@ __device__ __forceinline__ void consume_wide(State<KV, D> (&st)[RW], KBuf<KV, D>
   for (int r = 0; r < RW; ++r) {
     Probs<KV, D> P;
     softmax<KV, D, TAIL, true>(st[r], S[r], vb, P, cs + T::TPL * x.j, t1r[r], scale_log2, qop[r].bias);
-    pv_update<KV, D, TAIL>(st[r], vb, P, cs + T::TPL * x.j, x.t1);
+    pv_update<KV, D, TAIL, false>(st[r], vb, P, cs + T::TPL * x.j, x.t1);
   }
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
