@@ -447,6 +447,7 @@ def summarise(case: Case, t: dict, peak: float) -> dict:
         "step_GBps": round(case.step_bytes / step_us / 1e3, 1),
         "step_frac_of_peak": round(case.step_bytes / step_us / 1e3 / peak, 4),
         "kernel_us": {k: round(v["mean_us"], 2) for k, v in t.items() if isinstance(v, dict)},
+        "step_us_stats": {k: round(v, 2) for k, v in t["step"].items()},  # mean, median, p10, p90
         "dominant_kernel": "pa_decode_split" if case.split else "pa_decode",
         "dominant_GBps": round(dec_bytes / dec_us / 1e3, 1),
         "dominant_frac_of_peak": round(dec_bytes / dec_us / 1e3 / peak, 4),
@@ -644,6 +645,7 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": round(head["us_per_step"] / 1e3, 5),
         "us_per_step": head["us_per_step"],
+        "step_us_stats": head["step_us_stats"],
         "frac_of_hbm_peak": head["step_frac_of_peak"],
         "higher_is_better": True,
         "scaling": "weak",
