@@ -161,10 +161,9 @@ pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t n
  * sequence b then attends over its L = context_lens[b] cached tokens, the new
  * one included (the concatenation of page "字节跳动 AI Infra (2)", KV-cache
  * question, step-t equations).  The results (cache contents and out) are
- * those of the two calls, bit for bit.  With at most 16 query heads per kv
- * head it is one kernel (the append costs no launch of its own) for a bf16
- * or int8 cache, and for an int4 cache with at most 4 (sequence, kv head)
- * pairs per compute unit: the work-group of each (sequence, kv head) takes
+ * those of the two calls, bit for bit.  With a bf16, int8 or int4 cache and
+ * at most 16 query heads per kv head it is one kernel (the append costs no
+ * launch of its own): the work-group of each (sequence, kv head) takes
  * position L - 1's K and V from key/value (int8/int4: codes and scales,
  * quantised as the append quantises them; the bits the cache row receives)
  * and extra work-groups at the end of the grid write the rows.  Otherwise it

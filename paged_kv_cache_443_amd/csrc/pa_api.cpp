@@ -180,22 +180,13 @@ pa_status pa_append_decode(const void *key, const void *value, pa_dtype src_dtyp
   if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads > INT32_MAX) return PA_ERR_BAD_SHAPE;
   const int32_t group = num_heads / cache->num_kv_heads;
   // One kernel when every kv head has one work-group (at most 16 query heads
-  // per kv head): the units take the new row from the source (int8 / int4:
-  // quantised in the kernel exactly as the append does) and append
-  // work-groups at the end of the grid write the cache.  bf16 and int8 always
-  // (measured against two launches: 70B-shaped workload 80.4 -> 73.3 us,
-  // LLaMA-13B-shaped 272.1 -> 261.4 us, int8 391.7 -> 380.3 us).  int4 only
-  // with at most 4 (sequence, kv head) units per CU: its fused kernel holds
-  // one work-group per CU less (199 VGPRs against 165), which cost the
-  // int8-shaped int4 workload (8 units per CU) 237.8 -> 253.3 us.
-  bool fused = cache->kv_dtype != PA_F32 && group <= 16;
-  if (fused && cache->kv_dtype == PA_I4) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return from_hip(e);
-    fused = static_cast<int64_t>(num_seqs) * cache->num_kv_heads <= 4 * static_cast<int64_t>(cus);
-  }
+  // per kv head) and the cache is bf16, int8 or int4: the units take the new
+  // row from the source (int8 / int4: quantised in the kernel exactly as the
+  // append does) and append work-groups at the end of the grid write the
+  // cache (measured against two launches: 70B-shaped workload 80.0 -> 72.9
+  // us, LLaMA-13B-shaped 269.8 -> 261.4 us, int8 391.6 -> 379.9 us, int4
+  // 237.7 -> 231.2 us).
+  const bool fused = cache->kv_dtype != PA_F32 && group <= 16;
   if (!fused) {
     st = pa_reshape_and_cache(key, value, src_dtype, slot_mapping, num_seqs, cache, stream);
     if (st != PA_OK) return st;

@@ -128,6 +128,7 @@ struct Ctx {
   // scale (low half of news) and V scale (high half), fp16 bits
   int32_t newpos;
   uint32_t newk, newv, news;
+  uint8_t *scr;  // fused append: this wavefront's LDS merge slot, free while it streams
 };
 
 // K/V tile loads.  Tiles are read once per step and streamed past the caches
@@ -194,45 +195,39 @@ __device__ __forceinline__ void issue_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x
   for (int n = 0; n < T::ND; ++n) vb.v[n] = load_tile<NT>(vp + 16 * n);
 }
 
-// A row spread over the wavefront as in Ctx::newk: the 32 bits holding
-// channels c .. c + PERW - 1 as a storage vector holds them (bf16: 2 per
-// word; int8 codes: 4; int4 codes: 8, two per byte, the even channel in the
-// low nibble), c a multiple of PERW, and the element of channel c alone.
-template <int KV, int D>
-__device__ __forceinline__ uint32_t row_word(uint32_t mine, int c) {
-  if constexpr (KV == kBf16) {
-    if constexpr (D == 128)
-      return __shfl(mine, c >> 1);
-    else
-      return (__shfl(mine, c) & 0xffffu) | (__shfl(mine, c + 1) << 16);
-  } else if constexpr (KV == kInt8) {
-    if constexpr (D == 128)
-      return (__shfl(mine, c >> 1) & 0xffffu) | (__shfl(mine, (c >> 1) + 1) << 16);
-    else
-      return (__shfl(mine, c) & 0xffu) | ((__shfl(mine, c + 1) & 0xffu) << 8) |
-             ((__shfl(mine, c + 2) & 0xffu) << 16) | (__shfl(mine, c + 3) << 24);
-  } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // byte i: channels c + 2i (low nibble), c + 2i + 1
-      uint32_t byte;
-      if constexpr (D == 128)
-        byte = __shfl(mine, (c >> 1) + i) & 0xffu;
-      else
-        byte = (__shfl(mine, c + 2 * i) & 0xfu) | ((__shfl(mine, c + 2 * i + 1) & 0xfu) << 4);
-      w |= byte << (8 * i);
+// 32-bit words in one storage vector, and bits per element.
+template <int KV>
+constexpr int kVecWords = KV == kInt4 ? 2 : 4;
+template <int KV>
+constexpr int kElemBits = KV == kBf16 ? 16 : (KV == kInt8 ? 8 : 4);
+
+// The new row staged in the wavefront's LDS slot as a storage vector holds
+// it: K then V, D elements each (bf16 bits, int8 codes, or int4 codes two
+// per byte with the even channel in the low nibble).  Every lane writes its
+// channels (int4 at head_dim 64: even lanes write their pair's byte).
+template <int KV, int D, int BS>
+__device__ __forceinline__ void stage_new_row(const Ctx<KV, D, BS> &x, int lane) {
+  constexpr int RB = D * kElemBits<KV> / 8;  // bytes of one row
+  if constexpr (KV == kInt4 && D == 64) {
+    const uint32_t k2 = (x.newk & 0xfu) | ((__shfl_xor(x.newk, 1) & 0xfu) << 4);
+    const uint32_t v2 = (x.newv & 0xfu) | ((__shfl_xor(x.newv, 1) & 0xfu) << 4);
+    if ((lane & 1) == 0) {
+      x.scr[lane >> 1] = static_cast<uint8_t>(k2);
+      x.scr[RB + (lane >> 1)] = static_cast<uint8_t>(v2);
     }
-    return w;
+  } else {
+    constexpr int LB = RB / 64;  // bytes per lane: 1, 2 or 4
+    if constexpr (LB == 4) {
+      reinterpret_cast<uint32_t *>(x.scr)[lane] = x.newk;
+      reinterpret_cast<uint32_t *>(x.scr + RB)[lane] = x.newv;
+    } else if constexpr (LB == 2) {
+      reinterpret_cast<uint16_t *>(x.scr)[lane] = static_cast<uint16_t>(x.newk);
+      reinterpret_cast<uint16_t *>(x.scr + RB)[lane] = static_cast<uint16_t>(x.newv);
+    } else {
+      x.scr[lane] = static_cast<uint8_t>(x.newk);
+      x.scr[RB + lane] = static_cast<uint8_t>(x.newv);
+    }
   }
-}
-template <int KV, int D>
-__device__ __forceinline__ uint32_t row_elem(uint32_t mine, int c) {
-  constexpr int BITS = KV == kBf16 ? 16 : (KV == kInt8 ? 8 : 4);
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  if constexpr (D == 128)
-    return (__shfl(mine, c >> 1) >> (BITS * (c & 1))) & MASK;
-  else
-    return __shfl(mine, c) & MASK;
 }
 
 // Replace element e (ELEM-bit elements) of a vector of NW 32-bit words.
@@ -247,51 +242,52 @@ __device__ __forceinline__ void set_elem(Vec &v, int e, uint32_t val, bool hit) 
     if (hit && w == k) v[w] = (v[w] & ~mask) | ((val << sh) & mask);
 }
 
-// 32-bit words in one storage vector, and channels per word.
-template <int KV>
-constexpr int kVecWords = KV == kInt4 ? 2 : 4;
-template <int KV>
-constexpr int kElemBits = KV == kBf16 ? 16 : (KV == kInt8 ? 8 : 4);
-
 // K fragments of chunk cs: the lanes whose token is x.newpos take the new
-// row's channels (the bits the cache row will hold).  Every lane joins the
-// shuffles; the caller makes sure the chunk holds x.newpos (uniform).
+// row's channels from the staged row (the bits the cache row will hold).
 template <int KV, int D, int BS>
 __device__ __forceinline__ void patch_new_k(KBuf<KV, D> &kb, const Ctx<KV, D, BS> &x, int cs) {
   using T = Tile<KV, D>;
-  constexpr int PERW = 32 / kElemBits<KV>;  // channels per 32-bit word
+  using Vec = typename KvVec<KV>::T;
 #pragma unroll
-  for (int s = 0; s < T::NKL; ++s) {
-    const int c0 = T::X * (4 * s + x.j);  // this lane's vector: channels c0 .. c0 + X - 1
-    typename KvVec<KV>::T row;
+  for (int q = 0; q < T::NQ; ++q) {
+    const int t = cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3);
+    if (t == x.newpos) {
 #pragma unroll
-    for (int w = 0; w < kVecWords<KV>; ++w) row[w] = row_word<KV, D>(x.newk, c0 + PERW * w);
-#pragma unroll
-    for (int q = 0; q < T::NQ; ++q) {
-      const int t = cs + T::TPL * (x.m >> 2) + 4 * q + (x.m & 3);
-      if (t == x.newpos) kb.k[q][s] = row;
+      for (int s = 0; s < T::NKL; ++s)  // this lane's vector: channels X * (4s + j) ..
+        kb.k[q][s] = *reinterpret_cast<const Vec *>(x.scr + T::X * (4 * s + x.j) * kElemBits<KV> / 8);
     }
   }
 }
 
 // The V vectors of a lane group starting at tok0 (element newpos - tok0 of
-// channel m + 16n takes the new row's value) and, int8 / int4, the K and V
-// scales of that token.
+// channel m + 16n takes the staged row's value) and, int8 / int4, the K and
+// V scales of that token.
 template <int KV, int D, int BS>
 __device__ __forceinline__ void patch_new_v(VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x, int tok0) {
   using T = Tile<KV, D>;
+  constexpr int RB = D * kElemBits<KV> / 8;
   const int e = x.newpos - tok0;
-  const bool hit = e >= 0 && e < T::X;
+  if (e >= 0 && e < T::X) {
 #pragma unroll
-  for (int n = 0; n < T::ND; ++n)
-    set_elem<kElemBits<KV>, kVecWords<KV>>(vb.v[n], e, row_elem<KV, D>(x.newv, x.m + 16 * n), hit);
-  if constexpr (kQuant<KV>) {
-    // scales of tokens tok0 + 8i .. tok0 + 8i + 7 sit in ks[i] / vs[i]
+    for (int n = 0; n < T::ND; ++n) {
+      const int c = x.m + 16 * n;
+      uint32_t val;
+      if constexpr (KV == kBf16)
+        val = reinterpret_cast<const uint16_t *>(x.scr + RB)[c];
+      else if constexpr (KV == kInt8)
+        val = x.scr[RB + c];
+      else
+        val = (x.scr[RB + (c >> 1)] >> (4 * (c & 1))) & 0xfu;
+      set_elem<kElemBits<KV>, kVecWords<KV>>(vb.v[n], e, val, true);
+    }
+    if constexpr (kQuant<KV>) {
+      // scales of tokens tok0 + 8i .. tok0 + 8i + 7 sit in ks[i] / vs[i]
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool in = hit && (e >> 3) == i;
-      set_elem<16, 4>(vb.ks[i], e & 7, x.news & 0xffffu, in);
-      set_elem<16, 4>(vb.vs[i], e & 7, x.news >> 16, in);
+      for (int i = 0; i < 2; ++i) {
+        const bool in = (e >> 3) == i;
+        set_elem<16, 4>(vb.ks[i], e & 7, x.news & 0xffffu, in);
+        set_elem<16, 4>(vb.vs[i], e & 7, x.news >> 16, in);
+      }
     }
   }
 }
@@ -547,7 +543,10 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
   if constexpr (NEWROW) {
     static_assert(TAIL && !REFILL, "the new row is spliced into a chunk's tail");
     spliced = x.newpos >= cs && x.newpos < cs + T::CT;  // uniform over the wavefront
-    if (spliced) patch_new_k<KV, D, BS>(kb, x, cs);
+    if (spliced) {
+      stage_new_row<KV, D, BS>(x, threadIdx.x & 63);  // a wavefront's LDS accesses are performed in order
+      patch_new_k<KV, D, BS>(kb, x, cs);
+    }
   }
   qk<KV, D>(S, kb, qop);
   if constexpr (NEWROW) {
@@ -665,6 +664,9 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm.tbl;
+  // the wavefront's own merge slot (rows * (D + 4) floats >= 2 * D * 2 bytes):
+  // nothing reads or writes it until this wavefront has finished streaming
+  x.scr = reinterpret_cast<uint8_t *>(sm.acc + static_cast<size_t>(w) * rows * (D + 4));
 
   // end of the positions read: a causal group's last row sees nothing past
   // its own position (none at all when nq > L: t1 <= 0).  x.t1 is this
@@ -964,6 +966,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   x.newk = 0u;
   x.newv = 0u;
   x.news = 0u;
+  x.scr = nullptr;
 
   // this wavefront's rows end at its last group's last row (none: t1 = 0);
   // the unit's at its last wavefront's
@@ -1082,7 +1085,8 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
 // units splice them in.  SHARED: single-row-group units whose siblings read
 // the same K/V (ordinary loads, so the lines stay in the XCD's L2).
 template <int KV, int D, int BS, int NW, bool CAUSAL = false, int R = 1, bool FUSED = false, bool SHARED = false>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FUSED && KV == kInt4 ? 3 : 1)))
+void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, p.rows_per_group);
   const int HX = p.num_kv_heads * p.head_groups;
