@@ -24,7 +24,7 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;   // wavefronts per work-group
-constexpr int kUnroll = 8;  // partitions in flight per wavefront
+constexpr int kUnroll = 16;  // partitions in flight per wavefront
 
 template <int VEC>
 struct Vec;
