@@ -207,3 +207,49 @@ def test_fused_split_step_full_size_bitwise():
     assert torch.equal(pof.view(torch.int32), poa.view(torch.int32))
     assert torch.equal(plf.view(torch.int32), pla.view(torch.int32))
     assert _same_pools(cf, ca)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_fused_split_step_with_skipped_appends(kv):
+    """pa_append_decode_split with some appends skipped (slot -1, or past the
+    pool): those sequences read position L - 1 from the cache; partials equal
+    the two calls' bit for bit and the merge matches the oracle."""
+    w = make_custom(B=6, Hq=16, Hkv=2, D=128, bs=16, kv_dtype=kv, lengths=[40, 17, 300, 1, 64, 129], seed=33)
+    s = w.spec
+    P = 32
+    say(f"[fused split skipped] {kv} B={w.B}")
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    sl = sl.clone()
+    sl[1] = -1
+    sl[3] = w.num_blocks * s.bs + 5
+    sl[4] = -1
+    kn = kn * 50
+    vn = vn * 50
+    pmax = pa.max_partitions(tables.shape[1], s.bs, P)
+    B, Hq, D = q.shape
+    res = []
+    for fused in (True, False):
+        c = poisoned_cache(w)
+        gpu_append_tokens(w, c, include_last=True)
+        po = torch.full((B, Hq, pmax, D), float("nan"), dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, pmax), float("nan"), dtype=torch.float32, device=DEV)
+        if fused:
+            pa.append_decode_split(kn, vn, sl, q, c, tables, lens, s.scale, P, po, pl)
+        else:
+            pa.reshape_and_cache(kn, vn, sl, c)
+            pa.decode_split(q, c, tables, lens, s.scale, P, po, pl)
+        torch.cuda.synchronize()
+        res.append((c, po, pl))
+    (cf, pof, plf), (ca, poa, pla) = res
+    assert torch.equal(pof.view(torch.int32), poa.view(torch.int32))
+    assert torch.equal(plf.view(torch.int32), pla.view(torch.int32))
+    assert _same_pools(cf, ca)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    pa.reduce(pof, plf, lens, P, out)
+    torch.cuda.synchronize()
+    want = oracle.decode(w.q, oracle.build_cache(w), w.block_tables, w.context_lens, s.scale)
+    skipped = [1, 3, 4]
+    err = float(np.max(np.abs(out[skipped].cpu().numpy().astype(np.float64) - want[skipped])))
+    say(f"  skipped sequences: max abs err {err:.3e}")
+    assert err <= TOL[kv]
