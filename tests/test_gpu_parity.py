@@ -338,13 +338,14 @@ def test_side_stream_matches_default_stream():
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
-def test_graph_replays_match_eager(cfg):
-    """A decode step (append + decode, or append + split + merge) captured in a
-    HIP graph replays to the eager result every time, with eager work between
-    the replays."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_match_eager(cfg, fused):
+    """A decode step (append + decode, or append + split + merge; as separate
+    calls or as the fused calls) captured in a HIP graph replays to the eager
+    result every time, with eager work between the replays."""
     w = make_workload(cfg, small=True)
     s = w.spec
-    say(f"[graph] cfg{cfg} small")
+    say(f"[graph] cfg{cfg} small fused={fused}")
     cache = poisoned_cache(w)
     gpu_append_tokens(w, cache, include_last=False)
     from workloads.device import new_token_batch
@@ -358,12 +359,18 @@ def test_graph_replays_match_eager(cfg):
     out = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
 
     def step():
-        pa.reshape_and_cache(kn, vn, sl, cache)
-        if s.partition_size:
-            pa.decode_split(q, cache, tables, lens, s.scale, P, po, pl)
+        if fused and s.partition_size:
+            pa.append_decode_split(kn, vn, sl, q, cache, tables, lens, s.scale, P, po, pl)
             pa.reduce(po, pl, lens, P, out)
+        elif fused:
+            pa.append_decode(kn, vn, sl, q, cache, tables, lens, s.scale, out)
         else:
-            pa.decode(q, cache, tables, lens, s.scale, out)
+            pa.reshape_and_cache(kn, vn, sl, cache)
+            if s.partition_size:
+                pa.decode_split(q, cache, tables, lens, s.scale, P, po, pl)
+                pa.reduce(po, pl, lens, P, out)
+            else:
+                pa.decode(q, cache, tables, lens, s.scale, out)
 
     step()
     torch.cuda.synchronize()
