@@ -558,7 +558,7 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax<KV, D, TAIL, CAUSAL>(st, S, vb, P, cs + T::TPL * x.j, CAUSAL ? x.t1_row : x.t1, scale_log2, qop.bias);
-  pv_update<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  pv_update<KV, D, TAIL, KV != kInt4>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
     issue_v<NT>(vb, x, cn, idn);
