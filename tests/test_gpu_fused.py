@@ -1,5 +1,7 @@
 """pa_append_decode (one decode step in one call) vs pa_reshape_and_cache +
-pa_decode and vs the oracle, through the C ABI (needs an MI355X)."""
+pa_decode, and pa_append_decode_split vs pa_reshape_and_cache +
+pa_decode_split, bit for bit, and both vs the oracle, through the C ABI
+(needs an MI355X)."""
 import numpy as np
 import pytest
 import torch
