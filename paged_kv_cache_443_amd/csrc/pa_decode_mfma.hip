@@ -844,8 +844,10 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
 // launch's tail where CUs free up; split pass: every persistent work-group
 // writes its share after its last piece.  A wavefront writes
 // kAppendRowsPerWave (token, kv head) rows at a time: all the loads first,
-// then the stores.
-constexpr int kAppendRowsPerWave = 4;
+// then the stores.  One row per wavefront (more, shorter append work-groups)
+// measured 0.7-1 us faster on the 70B-shaped step than four, neutral
+// elsewhere.
+constexpr int kAppendRowsPerWave = 1;
 
 template <int KV, int D, int BS, int NW>
 __device__ __forceinline__ void append_rows(const DecodeParams &p, int first_wg, int nwg) {
