@@ -135,8 +135,11 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_
  * equations and PagedAttention kernel sketch).  L == 0 gives a zero row.
  *
  *   q             [num_seqs][num_heads][head_dim], q_dtype, 16-byte aligned
- *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past
- *                 ceil(L / block_size) are never read (may hold anything)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; the whole row must
+ *                 be readable memory.  Entries past ceil(L / block_size) may
+ *                 be loaded (the row is staged in LDS in windows, with no
+ *                 wait on L) but never form an address or influence the
+ *                 result: they may hold anything
  *   context_lens  int32 [num_seqs]
  *   out           [num_seqs][num_heads][head_dim], out_dtype, 16-byte aligned
  *   (q, kv, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16|F32),
@@ -336,7 +339,9 @@ pa_status pa_swap_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const i
  */
 typedef struct pa_block_manager pa_block_manager;
 
-/* Create a manager (host memory, owned by the caller until pa_bm_destroy). */
+/* Create a manager (host memory, owned by the caller until pa_bm_destroy).
+ * PA_ERR_BAD_SHAPE unless num_blocks >= 1, block_size >= 1 and
+ * num_blocks * block_size <= INT32_MAX (slots are int32). */
 pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager **out);
 void pa_bm_destroy(pa_block_manager *bm);
 /* Free blocks; references held on block b (-1 if b is out of range). */

@@ -36,6 +36,8 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager 
   if (out == nullptr) return PA_ERR_NULL_PTR;
   *out = nullptr;
   if (num_blocks < 1 || block_size < 1) return PA_ERR_BAD_SHAPE;
+  // slots (block * block_size + offset) are int32, as slot_mapping is
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return PA_ERR_BAD_SHAPE;
   pa_block_manager *bm = new (std::nothrow) pa_block_manager();
   if (bm == nullptr) return PA_ERR_OUT_OF_BLOCKS;
   try {
@@ -126,7 +128,8 @@ pa_status pa_bm_append_slot(pa_block_manager *bm, int32_t *table, int32_t *table
       copy_pair[1] = fresh;
     }
   }
-  *slot_out = table[j] * bs + off;
+  // in range: pa_bm_create bounds num_blocks * block_size by INT32_MAX
+  *slot_out = static_cast<int32_t>(static_cast<int64_t>(table[j]) * bs + off);
   return PA_OK;
 }
 

@@ -6,9 +6,20 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 namespace pa {
 namespace {
+
+// Dtype fields and arguments arrive from C callers as plain ints.  In C++
+// reading an enum object that holds a value outside its enumerators is
+// undefined, so validation reads them through their bytes.
+static_assert(sizeof(pa_dtype) == sizeof(int32_t), "pa_dtype is passed as a 32-bit int");
+int32_t raw(const pa_dtype &d) {
+  int32_t v;
+  std::memcpy(&v, &d, sizeof v);
+  return v;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -19,8 +30,7 @@ bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
 
 pa_status check_cache(const pa_kv_cache *c) {
   if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr) return PA_ERR_NULL_PTR;
-  if (c->kv_dtype != PA_F32 && c->kv_dtype != PA_BF16 && c->kv_dtype != PA_I8 && c->kv_dtype != PA_I4)
-    return PA_ERR_UNSUPPORTED;
+  if (raw(c->kv_dtype) < PA_F32 || raw(c->kv_dtype) > PA_I4) return PA_ERR_UNSUPPORTED;
   const bool want_scales = c->kv_dtype == PA_I8 || c->kv_dtype == PA_I4;
   if (want_scales && (c->k_scale == nullptr || c->v_scale == nullptr)) return PA_ERR_NULL_PTR;
   if (!want_scales && (c->k_scale != nullptr || c->v_scale != nullptr)) return PA_ERR_NULL_PTR;
@@ -40,8 +50,8 @@ pa_status check_append(const void *key, const void *value, pa_dtype src_dtype, c
   if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL_PTR;
-  const pa_dtype want = cache->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
-  if (src_dtype != want) return PA_ERR_UNSUPPORTED;
+  const int32_t want = cache->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
+  if (raw(src_dtype) != want) return PA_ERR_UNSUPPORTED;
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 4)) return PA_ERR_MISALIGNED;
   return PA_OK;
 }
@@ -57,16 +67,16 @@ pa_status check_decode_common(const void *q, pa_dtype q_dtype, int32_t num_seqs,
   if (static_cast<int64_t>(max_blocks_per_seq) * cache->block_size > INT32_MAX) return PA_ERR_BAD_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (q == nullptr || block_tables == nullptr || context_lens == nullptr) return PA_ERR_NULL_PTR;
-  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (raw(q_dtype) != PA_F32 && raw(q_dtype) != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4)) return PA_ERR_MISALIGNED;
   return PA_OK;
 }
 
 pa_status check_out(const void *out, pa_dtype q_dtype, pa_dtype kv_dtype, pa_dtype out_dtype) {
   if (out == nullptr) return PA_ERR_NULL_PTR;
-  const bool ok = (q_dtype == PA_F32 && kv_dtype == PA_F32 && out_dtype == PA_F32) ||
-                  (q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_I8 || kv_dtype == PA_I4) &&
-                   (out_dtype == PA_BF16 || out_dtype == PA_F32));
+  const int32_t qd = raw(q_dtype), kd = raw(kv_dtype), od = raw(out_dtype);
+  const bool ok = (qd == PA_F32 && kd == PA_F32 && od == PA_F32) ||
+                  (qd == PA_BF16 && (kd == PA_BF16 || kd == PA_I8 || kd == PA_I4) && (od == PA_BF16 || od == PA_F32));
   if (!ok) return PA_ERR_UNSUPPORTED;
   if (!aligned(out, 16)) return PA_ERR_MISALIGNED;
   return PA_OK;
@@ -109,7 +119,7 @@ pa_status check_reduce(const float *part_out, const float *part_lse, int32_t num
   if (num_seqs == 0) return PA_OK;
   if (part_out == nullptr || part_lse == nullptr || context_lens == nullptr || out == nullptr)
     return PA_ERR_NULL_PTR;
-  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (raw(out_dtype) != PA_F32 && raw(out_dtype) != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (!aligned(part_out, 16) || !aligned(part_lse, 4) || !aligned(context_lens, 4) || !aligned(out, 16))
     return PA_ERR_MISALIGNED;
   return PA_OK;

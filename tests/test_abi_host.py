@@ -87,6 +87,9 @@ def test_decode_rejections(L):
     assert _decode(L, c, qdt=PA_F32) == PA_ERR_UNSUPPORTED  # f32 q with a bf16 cache
     assert _decode(L, _cache(kv=PA_F32), odt=PA_BF16, qdt=PA_F32) == PA_ERR_UNSUPPORTED
     assert _decode(L, c, odt=PA_I8) == PA_ERR_UNSUPPORTED
+    # dtype arguments outside the enumerators (C callers pass plain ints)
+    assert _decode(L, c, qdt=9) == PA_ERR_UNSUPPORTED
+    assert _decode(L, c, odt=-1) == PA_ERR_UNSUPPORTED
     assert _decode(L, c, q=A16[4] + 8) == PA_ERR_MISALIGNED
     assert _decode(L, c, out=A16[7] + 4) == PA_ERR_MISALIGNED
     assert _decode(L, c, tables=A16[5] + 2) == PA_ERR_MISALIGNED
@@ -170,6 +173,7 @@ def test_reduce_rejections(L):
     assert _reduce(L, P=0) == PA_ERR_BAD_SHAPE
     assert _reduce(L, D=80) == PA_ERR_UNSUPPORTED
     assert _reduce(L, odt=PA_I8) == PA_ERR_UNSUPPORTED
+    assert _reduce(L, odt=17) == PA_ERR_UNSUPPORTED
     assert _reduce(L, po=A16[8] + 4) == PA_ERR_MISALIGNED
     assert _reduce(L, B=0, po=None, out=None) == PA_OK
 
@@ -187,6 +191,8 @@ def test_append_rejections(L):
     assert _append(L, _cache(kv=PA_F32), sdt=PA_BF16) == PA_ERR_UNSUPPORTED
     assert _append(L, _cache(kv=PA_I8), sdt=PA_F32) == PA_ERR_UNSUPPORTED
     assert _append(L, _cache(kv=PA_I4), sdt=PA_F32) == PA_ERR_UNSUPPORTED
+    assert _append(L, c, sdt=5) == PA_ERR_UNSUPPORTED
+    assert _append(L, _cache(kv=-3)) == PA_ERR_UNSUPPORTED
     assert _append(L, c, key=A16[10] + 4) == PA_ERR_MISALIGNED
     assert _append(L, c, slots=A16[12] + 1) == PA_ERR_MISALIGNED
     assert _append(L, c, T=0, key=None, value=None, slots=None) == PA_OK

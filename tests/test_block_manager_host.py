@@ -94,6 +94,9 @@ def test_c_abi_argument_checks():
     L = _lib.lib()
     h = ctypes.c_void_p()
     assert L.pa_bm_create(0, 16, ctypes.byref(h)) == PA_ERR_BAD_SHAPE
+    # slots are int32: a pool whose slot range overflows it is refused
+    assert L.pa_bm_create(2 ** 27, 16, ctypes.byref(h)) == PA_ERR_BAD_SHAPE
+    assert L.pa_bm_create(2 ** 26, 32, ctypes.byref(h)) == PA_ERR_BAD_SHAPE
     assert L.pa_bm_create(4, 16, None) == PA_ERR_NULL_PTR
     assert L.pa_bm_create(4, 16, ctypes.byref(h)) == PA_OK
     try:
