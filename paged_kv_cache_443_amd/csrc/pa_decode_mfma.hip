@@ -127,6 +127,7 @@ struct Ctx {
   // each, the lower channel in the low nibble); int8 / int4: the row's K
   // scale (low half of news) and V scale (high half), fp16 bits
   int32_t newpos;
+  int32_t newblk;  // fused append: the physical block slot_mapping names for the new row
   uint32_t newk, newv, news;
   uint8_t *scr;  // fused append: this wavefront's LDS merge slot, free while it streams
 };
@@ -542,7 +543,9 @@ __device__ __forceinline__ void consume(State<KV, D> &st, KBuf<KV, D> &kb, VBuf<
   bool spliced = false;
   if constexpr (NEWROW) {
     static_assert(TAIL && !REFILL, "the new row is spliced into a chunk's tail");
-    spliced = x.newpos >= cs && x.newpos < cs + T::CT;  // uniform over the wavefront
+    // uniform over the wavefront: the chunk holds the new position, and the
+    // table puts that position in the block the new row is written to
+    spliced = x.newpos >= cs && x.newpos < cs + T::CT && x.tbl[x.newpos / BS - x.lb0] == x.newblk;
     if (spliced) {
       stage_new_row<KV, D, BS>(x, threadIdx.x & 63);  // a wavefront's LDS accesses are performed in order
       patch_new_k<KV, D, BS>(kb, x, cs);
@@ -682,6 +685,7 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
   }
   x.nbv = (x.t1 + BS - 1) / BS;
   x.newpos = -1;
+  x.newblk = -1;
   x.newk = 0u;
   x.newv = 0u;
   x.news = 0u;
@@ -757,7 +761,15 @@ __device__ __forceinline__ void run_unit(const DecodeParams &p, const Smem &sm, 
       }
       x.news = static_cast<uint32_t>(qr.sk) | (static_cast<uint32_t>(qr.sv) << 16);
     }
-    if (valid) x.newpos = L - 1;
+    // The row is spliced in only where the cache receives it: slot_mapping[b]
+    // must be position L - 1's slot (its offset is checked here, its block
+    // against the staged table entry where the splice happens).  Otherwise
+    // position L - 1 is read from the cache, as pa_decode reads it after the
+    // append, and the append work-groups write the row where the slot says.
+    if (valid && arow.slot % BS == (L - 1) % BS) {
+      x.newpos = L - 1;
+      x.newblk = arow.slot / BS;
+    }
   }
 
   // ---- token range in windows of staged block-table entries (usually one) ----
@@ -965,6 +977,7 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = tbl;
   x.newpos = -1;  // no fused append on wide units
+  x.newblk = -1;
   x.newk = 0u;
   x.newv = 0u;
   x.news = 0u;

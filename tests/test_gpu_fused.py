@@ -255,3 +255,65 @@ def test_fused_split_step_with_skipped_appends(kv):
     err = float(np.max(np.abs(out[skipped].cpu().numpy().astype(np.float64) - want[skipped])))
     say(f"  skipped sequences: max abs err {err:.3e}")
     assert err <= TOL[kv]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
+def test_fused_step_with_a_slot_that_is_not_position_l_minus_1(kv):
+    """A slot that is not the table's slot of position L - 1 (a free block, or
+    a later offset of the last block): the fused step must not splice the row
+    in at L - 1 but read that position from the cache, as the two calls do."""
+    w = make_custom(B=5, Hq=16, Hkv=2, D=128, bs=16, kv_dtype=kv, lengths=[40, 17, 300, 70, 129], seed=28)
+    s = w.spec
+    say(f"[fused slot mismatch] {kv} B={w.B}")
+    q, tables, lens = meta(w)
+    kn, vn, sl = new_token_batch(w)
+    free = sorted(set(range(w.num_blocks)) - set(int(b) for b in w.used_blocks()))
+    assert free
+    sl = sl.clone()
+    sl[0] = free[0] * s.bs + 7                      # a block no sequence reads
+    L2 = int(w.context_lens[2])
+    assert (L2 - 1) % s.bs != s.bs - 1
+    sl[2] = int(w.block_tables[2][(L2 - 1) // s.bs]) * s.bs + (L2 - 1) % s.bs + 1  # a tail slot of the last block
+    sl[3] = free[-1] * s.bs + (int(w.context_lens[3]) - 1) % s.bs  # L - 1's offset in a free block
+    kn = kn * 50  # rows that would change the output if spliced in
+    vn = vn * 50
+    fused = poisoned_cache(w)
+    gpu_append_tokens(w, fused, include_last=True)
+    apart = poisoned_cache(w)
+    gpu_append_tokens(w, apart, include_last=True)
+    out_f = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    out_a = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    pa.append_decode(kn, vn, sl, q, fused, tables, lens, s.scale, out_f)
+    pa.reshape_and_cache(kn, vn, sl, apart)
+    pa.decode(q, apart, tables, lens, s.scale, out_a)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_a)
+    assert _same_pools(fused, apart)
+    # the sequences with mismatched slots decode over the cache as it was
+    want = oracle.decode(w.q, oracle.build_cache(w), w.block_tables, w.context_lens, w.spec.scale)
+    err = max_err(out_f[[0, 2, 3]], want[[0, 2, 3]])
+    say(f"  max abs err (mismatched rows) {err:.3e}")
+    assert err <= TOL[kv]
+    if kv == "i4":
+        return  # the int4 split step is two launches
+    # the fused split pass takes the same check
+    P = 64
+    pmax = pa.max_partitions(tables.shape[1], s.bs, P)
+    B, Hq, D = q.shape
+    res = []
+    for fuse in (True, False):
+        c = poisoned_cache(w)
+        gpu_append_tokens(w, c, include_last=True)
+        po = torch.full((B, Hq, pmax, D), float("nan"), dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, pmax), float("nan"), dtype=torch.float32, device=DEV)
+        if fuse:
+            pa.append_decode_split(kn, vn, sl, q, c, tables, lens, s.scale, P, po, pl)
+        else:
+            pa.reshape_and_cache(kn, vn, sl, c)
+            pa.decode_split(q, c, tables, lens, s.scale, P, po, pl)
+        res.append((c, po, pl))
+    torch.cuda.synchronize()
+    (cf, pof, plf), (ca, poa, pla) = res
+    assert torch.equal(pof.view(torch.int32), poa.view(torch.int32))
+    assert torch.equal(plf.view(torch.int32), pla.view(torch.int32))
+    assert _same_pools(cf, ca)
