@@ -3,25 +3,31 @@
 
 One step is one decode iteration of the whole path over a batch that is
 already resident in HBM: every sequence appends its newest K/V token to
-the paged cache (``pa_reshape_and_cache``), then attends over its cache
-(``pa_decode``, or ``pa_decode_split`` + ``pa_reduce`` for the long-context
-workload).  Before each timed step a 1 GiB read of a scratch buffer evicts
-the L2s and the 256 MB Infinity Cache with clean lines, so the K/V reads
-come from HBM and no write-back of earlier data lands inside the timed
-kernels.  Kernel times come from HIP events recorded on the stream the
-kernels run on (torch's current stream, which the binding launches on).
+the paged cache, then attends over its cache -- issued as a serving loop
+issues it, one ``pa_append_decode`` call (one fused kernel), or
+``pa_append_decode_split`` + ``pa_reduce`` for the long-context workload.
+Before each timed step a sequential read of a 1 GiB scratch buffer with the
+library's read probe (``pa_probe_read``, ordinary loads) evicts the L2s and
+the 256 MB Infinity Cache with clean lines, so the K/V reads come from HBM
+and no write-back of earlier data lands inside the timed kernels.  Kernel
+times come from HIP events recorded on the stream the kernels run on
+(torch's current stream, which the binding launches on).
 
-Printed: ONE JSON line.  ``value`` is the effective HBM rate of a step:
-algorithmic bytes (K/V of every cached token -- prefix-shared blocks
-once -- int8 scales, q, out, used block-table entries, context lengths,
-and the appended rows) divided by the step's kernel time.
+Printed: ONE JSON line.  The headline workload is the largest one, the
+INT8 KV-cache GQA decode plus cache append (256 sequences of 1024-8192
+tokens).  ``value`` is its effective HBM rate: algorithmic bytes (K/V of
+every cached token -- prefix-shared blocks once -- int8 scales, q, out,
+used block-table entries, context lengths, and the appended rows) divided
+by the median step time.  ``roofline`` reports the step's dominant kernel
+against the 8 TB/s HBM peak and against the probe's rate for the same tile
+pattern; every other workload carries the same block.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
-                  [--others 3,4,5] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5]
+                  [--others 2,3,4] [--no-cpu-baseline]
 
 The ``cpu_baseline`` leg times the fp64 CPU oracle (the parity reference,
 not a tuned CPU implementation) on one host core over a bounded sample of
-the same workload.
+the headline workload.
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged-decode attention µs/step + effective KV-read GB/s (% of HBM peak)"
-HEADLINE = 2
+HEADLINE = 5
 
 
 def log(msg: str) -> None:
@@ -51,10 +57,12 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5],
                     help="workload timed for the headline value")
-    ap.add_argument("--others", default="3,4,5",
-                    help="comma-separated workloads also timed and summarised ('' for none)")
+    ap.add_argument("--others", default="2,3,4",
+                    help="comma-separated workloads also timed and summarised ('' for none); the int8 "
+                         "workload's shapes with an int4 cache are added whenever workload 5 runs")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--probe-mib", type=int, default=2048, help="buffer of the read-bandwidth probe ('0': skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="upper bound on the oracle's timed CPU work")
@@ -130,15 +138,19 @@ class Case:
                              self.out)
 
     def kernels(self):
-        """The step's kernels as separate calls, by name (each is timed alone)."""
+        """The step's kernels, and the unfused calls, by name (each is timed alone)."""
         pa, s = self.pa, self.s
-        ks = {"append": lambda: pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)}
+        ks = {}
         if self.split:
+            ks["append_decode_split"] = lambda: pa.append_decode_split(
+                self.kn, self.vn, self.slots, self.q, self.cache, self.tables, self.lens, s.scale, s.partition_size,
+                self.part_out, self.part_lse)
+            ks["reduce"] = lambda: pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
             ks["decode_split"] = lambda: pa.decode_split(self.q, self.cache, self.tables, self.lens, s.scale,
                                                          s.partition_size, self.part_out, self.part_lse)
-            ks["reduce"] = lambda: pa.reduce(self.part_out, self.part_lse, self.lens, s.partition_size, self.out)
         else:
             ks["decode"] = lambda: pa.decode(self.q, self.cache, self.tables, self.lens, s.scale, self.out)
+        ks["append"] = lambda: pa.reshape_and_cache(self.kn, self.vn, self.slots, self.cache)
         return ks
 
     def decode_f32(self):
@@ -161,19 +173,24 @@ class Case:
 
 
 class Flush:
-    """Evicts the L2s and the Infinity Cache by reading a 1 GiB buffer.
+    """Evicts the L2s and the Infinity Cache: one sequential pass of the
+    library's read probe (ordinary loads) over a 1 GiB buffer, which leaves
+    the caches holding clean lines only."""
 
-    A float32 sum into a float32 scalar: one read pass, no temporaries and no
-    dtype conversion, so the caches are left holding clean lines only.
-    """
-
-    def __init__(self, torch, mib: int, device):
-        self.torch = torch
-        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=device)
-        self.sink = torch.zeros((), dtype=torch.float32, device=device)
+    def __init__(self, torch, pa, mib: int, device):
+        self.pa = pa
+        self.buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.int32, device=device)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=device)
 
     def __call__(self):
-        self.torch.sum(self.buf, dim=0, out=self.sink)
+        self.pa.probe_read(self.buf, "seq", self.sink)
+
+
+def stats_us(v) -> dict:
+    """mean, median, p10, p90 of durations in ms, as microseconds."""
+    v = sorted(v)
+    return {"mean_us": 1e3 * sum(v) / len(v), "median_us": 1e3 * v[len(v) // 2],
+            "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
 
 
 def _timed(torch, fn, steps: int, warmup: int, flush) -> list:
@@ -201,16 +218,49 @@ def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
     t0 = time.perf_counter()
     step = _timed(torch, case.step, steps, warmup, flush)
     wall = time.perf_counter() - t0
-
-    def stats(v):
-        v = sorted(v)
-        return {"mean_us": 1e3 * sum(v) / len(v), "median_us": 1e3 * v[len(v) // 2],
-                "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
-
-    r = {"step": stats(step), "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
+    r = {"step": stats_us(step), "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
     for name, fn in case.kernels().items():
-        r[name] = stats(_timed(torch, fn, steps, warmup, flush))
+        r[name] = stats_us(_timed(torch, fn, steps, warmup, flush))
     return r
+
+
+# --------------------------------------------------------------------------
+# read-bandwidth probe (the achievable HBM read rate for each access pattern)
+# --------------------------------------------------------------------------
+
+
+def probe_pattern(s) -> tuple:
+    """The probe pattern of a workload's K/V gather: one (block, kv head) tile
+    of K, read as the decode kernel reads it (non-temporal for bf16 tiles,
+    ordinary loads for quantised ones)."""
+    elem = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[s.kv_dtype]
+    tile = int(s.bs * s.D * elem)
+    return ("tiles_nt" if s.kv_dtype in ("bf16", "f32") else "tiles", tile)
+
+
+def run_probe(torch, pa, mib: int, steps: int, flush, patterns) -> dict:
+    """Median read rate of pa_probe_read over a ``mib`` MiB buffer: one
+    sequential pass (ordinary and non-temporal loads) and each (mode, tile
+    bytes) pattern, the caches flushed before each pass."""
+    dev = torch.device("cuda:0")
+    buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {"buffer_mib": mib}
+    todo = [("seq", 0), ("seq_nt", 0)] + sorted(set(patterns))
+    for mode, tile in todo:
+        nbytes = {}
+
+        def run():
+            nbytes["n"] = pa.probe_read(buf, mode, sink, tile_bytes=tile or 4096)
+
+        t = stats_us(_timed(torch, run, steps, 3, flush))
+        key = mode if not tile else f"{mode}_{tile}"
+        res[key] = {"GBps": round(nbytes["n"] / t["median_us"] / 1e3, 1), "bytes": nbytes["n"],
+                    "median_us": round(t["median_us"], 2)}
+        log(f"probe {key}: {res[key]}")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_copy_blocks(case: Case, steps: int, warmup: int, flush, max_pairs: int = 1024) -> dict:
@@ -238,10 +288,10 @@ def time_copy_blocks(case: Case, steps: int, warmup: int, flush, max_pairs: int 
         pa.copy_blocks(case.cache, dev_pairs)
         b.record()
     torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
     s = case.s
-    elem = {"f32": 4, "bf16": 2, "i8": 1}[s.kv_dtype]
-    per_block = s.Hkv * s.bs * s.D * elem * 2 + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype == "i8" else 0)
+    elem = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[s.kv_dtype]
+    per_block = int(s.Hkv * s.bs * s.D * elem * 2) + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype in ("i8", "i4") else 0)
     moved = n * per_block * 2 + n * 8  # read and written, plus the pairs
     return {"pairs": n, "bytes": moved, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}
 
@@ -275,7 +325,7 @@ def time_multi(case: Case, steps: int, warmup: int, flush, perfmodel, q_len: int
         run()
         b.record()
     torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
     nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs,
                                    kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
                                    out_dtype="bf16" if case.out_dtype == torch.bfloat16 else "f32")
@@ -314,9 +364,9 @@ def time_swap(case: Case, steps: int, warmup: int, max_pairs: int = 1024) -> dic
             pa.swap_blocks(a, b, pairs)
             e1.record()
         torch.cuda.synchronize()
-        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
-        elem = {"f32": 4, "bf16": 2, "i8": 1}[s.kv_dtype]
-        per_block = s.Hkv * s.bs * s.D * elem * 2 + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype == "i8" else 0)
+        us = stats_us([e0.elapsed_time(e1) for e0, e1 in ev])["median_us"]
+        elem = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[s.kv_dtype]
+        per_block = int(s.Hkv * s.bs * s.D * elem * 2) + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype in ("i8", "i4") else 0)
         res[name] = {"us": round(us, 2), "GBps": round(n * per_block / us / 1e3, 1)}
     res.update({"pairs": n, "bytes_each_way": n * per_block})
     del host
@@ -364,7 +414,7 @@ def time_multi_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush
         run()
         b.record()
     torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
     nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype="bf16",
                                    q_dtype="bf16", out_dtype="bf16")
     flops = perfmodel.multi_flops(w.context_lens, counts, Hq=Hq, D=128)
@@ -422,7 +472,7 @@ def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flus
             run()
             b.record()
         torch.cuda.synchronize()
-        return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+        return stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
 
     us, us_split = timed(single), timed(split)
     nbytes = perfmodel.decode_bytes(w.context_lens, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype=kv, q_dtype="bf16",
@@ -435,41 +485,69 @@ def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flus
             "split_512_plus_merge_us": round(us_split, 2), "split_frac_of_hbm_peak": frac(us_split)}
 
 
-def summarise(case: Case, t: dict, peak: float) -> dict:
+def summarise(case: Case, t: dict, peak: float, probe: dict) -> dict:
+    """A workload's line: the step (median and spread), every kernel timed
+    alone, and the roofline block of the step's dominant kernel."""
     s = case.s
-    step_us = t["step"]["mean_us"]
-    key = "decode_split" if case.split else "decode"
-    dec_us = t[key]["mean_us"]
-    dec_bytes = case.split_kernel_bytes if case.split else case.decode_bytes
-    d = {
+    step = t["step"]
+    med = step["median_us"]
+    if case.split:
+        # append + split pass in one kernel, then the merge
+        dom_name, dom = "pa_append_decode_split", t["append_decode_split"]
+        dom_bytes = case.split_kernel_bytes + case.append_bytes
+    else:
+        # the step is one pa_append_decode call: one fused kernel for these workloads
+        dom_name, dom = "pa_append_decode", step
+        dom_bytes = case.step_bytes
+    achieved = dom_bytes / dom["mean_us"] / 1e3
+    mode, tile = probe_pattern(s)
+    pkey = f"{mode}_{tile}"
+    probe_gbps = probe.get(pkey, {}).get("GBps") if probe else None
+    traffic = measured_traffic(s.name)
+    roofline = {
+        "bound": "hbm",
+        "kernel": dom_name,
+        "achieved": round(achieved, 1),
+        "peak": peak,
+        "unit": "GB/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic["bytes"] if traffic else None,
+        "algorithmic_bytes_per_launch": dom_bytes,
+        "avg_launch_us": round(dom["mean_us"], 2),
+        "median_launch_us": round(dom["median_us"], 2),
+        "probe_pattern": pkey,
+        "probe_GBps": probe_gbps,
+        "frac_of_probe": round(achieved / probe_gbps, 4) if probe_gbps else None,
+    }
+    if traffic:
+        roofline["traffic_source"] = traffic["source"]
+        roofline["traffic_over_algorithmic"] = round(traffic["bytes"] / dom_bytes, 4)
+    return {
         "workload": s.name,
-        "us_per_step": round(step_us, 2),
-        "step_GBps": round(case.step_bytes / step_us / 1e3, 1),
-        "step_frac_of_peak": round(case.step_bytes / step_us / 1e3 / peak, 4),
-        "kernel_us": {k: round(v["mean_us"], 2) for k, v in t.items() if isinstance(v, dict)},
-        "step_us_stats": {k: round(v, 2) for k, v in t["step"].items()},  # mean, median, p10, p90
-        "dominant_kernel": "pa_decode_split" if case.split else "pa_decode",
-        "dominant_GBps": round(dec_bytes / dec_us / 1e3, 1),
-        "dominant_frac_of_peak": round(dec_bytes / dec_us / 1e3 / peak, 4),
+        "us_per_step": round(med, 2),
+        "step_GBps": round(case.step_bytes / med / 1e3, 1),
+        "step_frac_of_peak": round(case.step_bytes / med / 1e3 / peak, 4),
+        "step_us_stats": {k: round(v, 2) for k, v in step.items()},  # mean, median, p10, p90
+        "kernel_mean_us": {k: round(v["mean_us"], 2) for k, v in t.items() if isinstance(v, dict)},
+        "kernel_median_us": {k: round(v["median_us"], 2) for k, v in t.items() if isinstance(v, dict)},
+        "roofline": roofline,
         "bytes": {"step": case.step_bytes, "decode": case.decode_bytes,
                   "decode_logical": case.decode_bytes_logical, "append": case.append_bytes,
                   "split_scratch_overhead": case.scratch_bytes},
     }
-    traffic = measured_traffic(s.name)
-    d["dominant_traffic_bytes"] = traffic["bytes"] if traffic else None
-    return d
 
 
 # --------------------------------------------------------------------------
 # HBM traffic of the dominant kernel (from rocprofv3 counter passes)
 # --------------------------------------------------------------------------
 
-KERNEL_SOURCES = ("pa_decode_mfma.hip", "pa_device.h")
+KERNEL_SOURCES = ("pa_decode_mfma.hip", "pa_device.h", "pa_append_row.h")
 
 
 def kernel_source_hash() -> str:
     """sha256 over what the decode kernels are built from: their source file,
-    the device helpers and the parameter struct they take."""
+    the device helpers, the append row code the fused kernels share and the
+    parameter struct they take."""
     import hashlib
     import re
 
@@ -510,28 +588,31 @@ def measured_traffic(workload: str):
 # --------------------------------------------------------------------------
 
 
-def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32, min_s: float = 10.0) -> dict:
-    """The oracle on one host core over the timed workload's sequences, in
-    order, until ``budget_s`` of work; when the whole batch takes less than
-    ``min_s`` it is passed over again until ``min_s`` (the rate counts every
-    sequence decoded; parity is checked on the first pass)."""
+def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32, min_s: float = 10.0,
+                 max_seqs: int = 40) -> dict:
+    """The oracle on one host core over a bounded sample of the timed
+    workload: its first ``max_seqs`` sequences (the oracle's cache is built
+    for those only, untimed), decoded in order until ``budget_s`` of work, and
+    passed over again until ``min_s`` when one pass is shorter (the rate
+    counts every sequence decoded; parity is checked on the first pass)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
 
     w, s = case.w, case.s
+    n = min(w.B, max_seqs)
     host_cores = os.cpu_count()
     allowed = sorted(os.sched_getaffinity(0))
-    log("cpu baseline: building the oracle's cache (not timed)")
-    oc = oracle.build_cache(w)
+    log(f"cpu baseline: building the oracle's cache for {n} sequences (not timed)")
+    oc = oracle.build_cache(w, seqs=range(n))
     os.sched_setaffinity(0, {allowed[0]})
     done, work, secs, toks, errs, passes = [], [], 0.0, 0, [], 0
     try:
         with threadpool_limits(limits=1):
             while secs < min_s and secs < budget_s:
                 passes += 1
-                for b in range(w.B):
+                for b in range(n):
                     sl = [b]
                     t0 = time.perf_counter()
                     want = oracle.decode(w.q[sl], oc, w.block_tables[sl], w.context_lens[sl], s.scale)
@@ -554,9 +635,8 @@ def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32, min_s: flo
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"oracle.decode (numpy fp64) over sequences 0..{done[-1]} of {w.B} ({toks} cached tokens, "
-                   f"{len(done)}/{w.B} of the batch) of the timed workload, {passes} pass(es), "
-                   f"one host core of {host_cores}"),
+        "sample": (f"oracle.decode (numpy fp64) over sequences 0..{done[-1]} of {w.B} ({toks} cached tokens) of "
+                   f"the timed workload, {passes} pass(es), one host core of {host_cores}"),
         "seconds": round(secs, 2),
         "us_per_step_equiv": round(secs * 1e6 * w.total_tokens() / max(work_tokens, 1), 1),
         "parity_max_abs_err_vs_gpu_fp32_out": max(errs) if errs else None,
@@ -580,6 +660,7 @@ def main(argv=None) -> int:
 
     import paged_kv_cache_443_amd as pa
     from paged_kv_cache_443_amd import _lib, perfmodel
+    from workloads import CONFIGS
 
     if not torch.cuda.is_available():
         log("no GPU visible")
@@ -588,7 +669,7 @@ def main(argv=None) -> int:
     peak = perfmodel.HBM_PEAK_GBPS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    flush = Flush(torch, args.flush_mib, dev)
+    flush = Flush(torch, pa, args.flush_mib, dev)
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.int32, device=dev)
@@ -600,15 +681,24 @@ def main(argv=None) -> int:
 
     others = [int(c) for c in args.others.split(",") if c.strip()] if args.others else []
     others = [c for c in others if c != args.config]
+    runs = [args.config] + others
+
+    # read-bandwidth probe for every workload's tile pattern
+    probe = {}
+    if args.probe_mib > 0:
+        pats = [probe_pattern(CONFIGS[c]) for c in runs]
+        if 5 in runs:
+            pats.append(probe_pattern(type(CONFIGS[5])(**{**CONFIGS[5].__dict__, "kv_dtype": "i4"})))
+        probe = run_probe(torch, pa, args.probe_mib, min(args.steps, 20), flush, pats)
 
     # headline workload
     case = Case(args.config, args.seed, torch, pa, perfmodel)
     log(f"timing cfg{args.config}: {args.warmup} warmup + {args.steps} steps")
     t = time_case(case, args.steps, args.warmup, flush)
-    head = summarise(case, t, peak)
-    log(f"cfg{args.config}: {head['us_per_step']} us/step, {head['step_GBps']} GB/s "
+    head = summarise(case, t, peak, probe)
+    log(f"cfg{args.config}: {head['us_per_step']} us/step (median), {head['step_GBps']} GB/s "
         f"({100 * head['step_frac_of_peak']:.1f}% of {peak:.0f}); dominant kernel "
-        f"{head['dominant_GBps']} GB/s")
+        f"{head['roofline']['achieved']} GB/s")
     out32 = case.decode_f32().cpu().numpy()
     copy_stats = time_copy_blocks(case, args.steps, args.warmup, flush)
     log(f"copy_blocks: {copy_stats}")
@@ -618,24 +708,6 @@ def main(argv=None) -> int:
     log(f"decode_multi: {multi_stats}")
 
     s = case.s
-    dec_key = "decode_split" if case.split else "decode"
-    dec_bytes = case.split_kernel_bytes if case.split else case.decode_bytes
-    dec_us = t[dec_key]["mean_us"]
-    traffic = measured_traffic(s.name)
-    roofline = {
-        "bound": "hbm",
-        "kernel": head["dominant_kernel"],
-        "achieved": round(dec_bytes / dec_us / 1e3, 1),
-        "peak": peak,
-        "unit": "GB/s",
-        "frac": round(dec_bytes / dec_us / 1e3 / peak, 4),
-        "traffic": traffic["bytes"] if traffic else None,
-        "algorithmic_bytes_per_launch": dec_bytes,
-        "avg_launch_us": round(dec_us, 2),
-    }
-    if traffic:
-        roofline["traffic_source"] = traffic["source"]
-
     line = {
         "metric": METRIC,
         "value": head["step_GBps"],
@@ -650,7 +722,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": s.kv_dtype if s.kv_dtype != "i8" else "i8",
+        "dtype": s.kv_dtype,
         "data": "synthetic",
         "config": {
             "workload": s.name,
@@ -658,9 +730,11 @@ def main(argv=None) -> int:
             "kv_dtype": s.kv_dtype, "q_out_dtype": s.q_dtype, "cached_tokens": case.w.total_tokens(),
             "partition_size": s.partition_size, "seed": case.w.seed,
         },
-        "kernel_us": head["kernel_us"],
+        "kernel_mean_us": head["kernel_mean_us"],
+        "kernel_median_us": head["kernel_median_us"],
         "bytes_per_step": head["bytes"],
-        "roofline": roofline,
+        "roofline": head["roofline"],
+        "probe": probe,
         "copy_blocks": copy_stats,
         "swap_blocks": swap_stats,
         "decode_multi": multi_stats,
@@ -685,22 +759,18 @@ def main(argv=None) -> int:
         line["decode_mqa"] = mqa
 
     other = {}
-    for c in others:
-        oc = Case(c, None, torch, pa, perfmodel)
-        log(f"timing cfg{c}")
-        ot = time_case(oc, args.steps, args.warmup, flush)
-        other[f"cfg{c}"] = summarise(oc, ot, peak)
-        log(f"cfg{c}: {other[f'cfg{c}']['us_per_step']} us/step, {other[f'cfg{c}']['step_GBps']} GB/s")
-        oc.free()
-        del oc
-        torch.cuda.empty_cache()
-    if "5" in [str(c) for c in others]:
+    extra = [(c, {}) for c in others]
+    if 5 in runs:
         # the int8 workload's shapes with an int4 cache (the other quantised KV format)
-        oc = Case(5, None, torch, pa, perfmodel, kv_dtype="i4", name="int4kv-gqa-append")
-        log("timing cfg5 with an int4 cache")
+        extra.append((5, {"kv_dtype": "i4", "name": "int4kv-gqa-append"}))
+    for c, kw in extra:
+        key = f"cfg{c}" + ("-int4" if kw else "")
+        oc = Case(c, None, torch, pa, perfmodel, **kw)
+        log(f"timing {key}")
         ot = time_case(oc, args.steps, args.warmup, flush)
-        other["cfg5-int4"] = summarise(oc, ot, peak)
-        log(f"cfg5-int4: {other['cfg5-int4']['us_per_step']} us/step, {other['cfg5-int4']['step_GBps']} GB/s")
+        other[key] = summarise(oc, ot, peak, probe)
+        log(f"{key}: {other[key]['us_per_step']} us/step, {other[key]['step_GBps']} GB/s, dominant kernel "
+            f"{other[key]['roofline']['frac']:.3f} of peak")
         oc.free()
         del oc
         torch.cuda.empty_cache()

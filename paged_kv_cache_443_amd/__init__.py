@@ -29,6 +29,7 @@ __all__ = [
     "decode_split",
     "reduce",
     "split_workspace_bytes",
+    "probe_read",
     "max_partitions",
     "copy_blocks",
     "swap_blocks",
@@ -285,6 +286,29 @@ def reduce(part_out: torch.Tensor, part_lse: torch.Tensor, context_lens: torch.T
                               _ptr(out), _DT[out.dtype], _stream(out.device))
     _check("pa_reduce", st)
     return out
+
+
+PROBE_MODES = {"seq": 0, "seq_nt": 1, "tiles": 2, "tiles_nt": 3}
+
+
+def probe_read(buf: torch.Tensor, mode: str, sink: torch.Tensor, tile_bytes: int = 4096) -> int:
+    """Read ``buf`` (a contiguous GPU tensor) once with the library's HBM read probe; returns the bytes read.
+
+    ``mode``: "seq" / "seq_nt" (one sequential pass, ordinary / non-temporal loads) or "tiles" /
+    "tiles_nt" (whole ``tile_bytes`` tiles in a scattered order, the largest power-of-two count that
+    fits).  ``sink`` is a one-element int32 GPU tensor that keeps the loads live."""
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32)
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    st = _lib.lib().pa_probe_read(_ptr(buf), nbytes, PROBE_MODES[mode], int(tile_bytes), _ptr(sink),
+                                  _stream(buf.device))
+    _check("pa_probe_read", st)
+    if mode.startswith("seq"):
+        return nbytes
+    n = 1
+    while n * 2 * tile_bytes <= nbytes:
+        n *= 2
+    return n * tile_bytes
 
 
 def split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_num_partitions: int) -> int:

@@ -43,6 +43,7 @@ EXPORTED = (
     "pa_bm_fork",
     "pa_bm_append_slot",
     "pa_split_workspace_bytes",
+    "pa_probe_read",
     "pa_status_string",
     "pa_last_hip_error",
 )
@@ -121,6 +122,8 @@ def lib() -> ctypes.CDLL:
     L.pa_bm_append_slot.restype = c_int
     L.pa_split_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32]
     L.pa_split_workspace_bytes.restype = c_size_t
+    L.pa_probe_read.argtypes = [c_void_p, c_size_t, c_int32, c_int32, c_void_p, c_void_p]
+    L.pa_probe_read.restype = c_int
     L.pa_status_string.argtypes = [c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_hip_error.argtypes = []

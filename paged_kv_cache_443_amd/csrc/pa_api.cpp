@@ -8,6 +8,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_probe.h"
 #include "pa_validate.h"
 
 namespace {
@@ -301,6 +302,13 @@ pa_status pa_swap_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const i
   pa_status st = pa::check_swap(src, dst, block_pairs, num_pairs);
   if (st != PA_OK || num_pairs == 0) return st;
   return launch_block_copies(src, dst, block_pairs, num_pairs, stream);
+}
+
+pa_status pa_probe_read(const void *buf, size_t bytes, int32_t mode, int32_t tile_bytes, uint32_t *sink,
+                        hipStream_t stream) {
+  const pa_status st = pa::check_probe(buf, bytes, mode, tile_bytes, sink);
+  if (st != PA_OK) return st;
+  return from_hip(pa::launch_probe_read(buf, bytes, mode, tile_bytes, sink, stream));
 }
 
 size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {

@@ -105,5 +105,6 @@ hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
+hipError_t launch_probe_read(const void *buf, size_t bytes, int mode, int tile_bytes, uint32_t *sink, hipStream_t s);
 
 }  // namespace pa

@@ -150,6 +150,16 @@ pa_status check_swap(const pa_kv_cache *src, const pa_kv_cache *dst, const int32
   return PA_OK;
 }
 
+pa_status check_probe(const void *buf, size_t bytes, int32_t mode, int32_t tile_bytes, const uint32_t *sink) {
+  if (buf == nullptr || sink == nullptr) return PA_ERR_NULL_PTR;
+  if (mode < 0 || mode > 3) return PA_ERR_UNSUPPORTED;
+  if (bytes < 16 || bytes % 16 != 0) return PA_ERR_BAD_SHAPE;
+  if (mode >= 2 && (tile_bytes < 16 || tile_bytes % 16 != 0 || static_cast<size_t>(tile_bytes) > bytes))
+    return PA_ERR_BAD_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
 size_t split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
   if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_num_partitions < 1) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * max_num_partitions;

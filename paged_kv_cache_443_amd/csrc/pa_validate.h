@@ -25,6 +25,7 @@ pa_status check_reduce(const float *part_out, const float *part_lse, int32_t num
                        int32_t partition_size, const void *out, pa_dtype out_dtype);
 pa_status check_copy(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs);
 pa_status check_swap(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *block_pairs, int32_t num_pairs);
+pa_status check_probe(const void *buf, size_t bytes, int32_t mode, int32_t tile_bytes, const uint32_t *sink);
 size_t split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions);
 
 }  // namespace pa
