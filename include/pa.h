@@ -21,7 +21,9 @@
  *   frees nothing of the caller's, copies nothing to the host and never
  *   synchronises; it keeps no state except a thread-local copy of the last
  *   HIP error.  (The host block manager's bookkeeping lives in host memory
- *   that pa_bm_create allocates and pa_bm_destroy frees.)
+ *   that pa_bm_create allocates and pa_bm_destroy frees; the one fixed
+ *   device array of pa_decode_split_noalloc is part of the library's code
+ *   object, not an allocation, and its address is looked up once per GPU.)
  * - Every call validates its host-visible arguments, then enqueues its
  *   kernels on `stream` and returns.  PA_OK means "valid and launched", not
  *   "finished".  On an error status nothing is launched and no output is
@@ -273,6 +275,34 @@ pa_status pa_decode_split(const void *q, pa_dtype q_dtype, int32_t num_seqs, int
 pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_seqs, int32_t num_heads,
                     int32_t head_dim, int32_t max_num_partitions, const int32_t *context_lens,
                     int32_t partition_size, void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_decode_split_noalloc -- pa_decode_split followed by pa_reduce, with the
+ * partials in the library's own device memory instead of a caller workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The call
+ * allocates nothing.  Arguments as for pa_decode_split up to partition_size,
+ * then out / out_dtype as for pa_decode.  It uses max_num_partitions =
+ * ceil(max_blocks_per_seq * block_size / partition_size), and the result is
+ * that of pa_decode_split with that max_num_partitions followed by pa_reduce,
+ * bit for bit.
+ *
+ * Scratch: one fixed array of 32 MiB per GPU (a file-scope device array of
+ * the library, held by every GPU the library runs on until the process
+ * ends).  It must hold num_seqs * num_heads * max_num_partitions * (head_dim
+ * floats of partial output, placed first and padded to 256 bytes, then one
+ * float of lse): pa_split_workspace_bytes() of those sizes <= 32 MiB, else
+ * PA_ERR_BAD_WORKSPACE and nothing is launched.  Every call on a GPU uses
+ * the same array and leaves its partials there: calls that overlap on one
+ * GPU (on different streams without ordering between them) race and give
+ * undefined results.  Calls ordered on one stream are safe.
+ * Preconditions (device data): those of pa_decode_split.
+ */
+pa_status pa_decode_split_noalloc(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                                  const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, float scale, int32_t partition_size, void *out,
+                                  pa_dtype out_dtype, hipStream_t stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks (the copy of copy-on-write).

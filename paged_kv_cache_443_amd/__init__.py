@@ -27,6 +27,7 @@ __all__ = [
     "append_decode_split",
     "decode_multi",
     "decode_split",
+    "decode_split_noalloc",
     "reduce",
     "split_workspace_bytes",
     "probe_read",
@@ -272,6 +273,21 @@ def decode_split(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, co
                                     block_tables.shape[1], _ptr(context_lens), float(scale), int(partition_size),
                                     Pmax, _ptr(part_out), _ptr(part_lse), _stream(q.device))
     _check("pa_decode_split", st)
+
+
+def decode_split_noalloc(q: torch.Tensor, cache: KVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         scale: float, partition_size: int, out: torch.Tensor) -> torch.Tensor:
+    """KV-split decode (split pass + merge) into ``out`` ``[B, Hq, D]`` with the partials in the library's
+    own fixed device scratch (32 MiB per GPU): no workspace argument and no allocation.  Calls that
+    overlap on one GPU race on that scratch."""
+    B, Hq, D = _decode_args(q, cache, block_tables, context_lens)
+    _need(out, "out", (torch.float32, torch.bfloat16), (B, Hq, D))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_decode_split_noalloc(_ptr(q), _DT[q.dtype], B, Hq, ctypes.byref(desc), _ptr(block_tables),
+                                            block_tables.shape[1], _ptr(context_lens), float(scale),
+                                            int(partition_size), _ptr(out), _DT[out.dtype], _stream(q.device))
+    _check("pa_decode_split_noalloc", st)
+    return out
 
 
 def reduce(part_out: torch.Tensor, part_lse: torch.Tensor, context_lens: torch.Tensor, partition_size: int,

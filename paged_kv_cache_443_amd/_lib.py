@@ -31,6 +31,7 @@ EXPORTED = (
     "pa_append_decode_split",
     "pa_decode_multi",
     "pa_decode_split",
+    "pa_decode_split_noalloc",
     "pa_reduce",
     "pa_copy_blocks",
     "pa_swap_blocks",
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_split.argtypes = [c_void_p, c_int, c_int32, c_int32, P, c_void_p, c_int32, c_void_p, c_float,
                                   c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     L.pa_decode_split.restype = c_int
+    L.pa_decode_split_noalloc.argtypes = [c_void_p, c_int, c_int32, c_int32, P, c_void_p, c_int32, c_void_p, c_float,
+                                          c_int32, c_void_p, c_int, c_void_p]
+    L.pa_decode_split_noalloc.restype = c_int
     L.pa_reduce.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                             c_int, c_void_p]
     L.pa_reduce.restype = c_int

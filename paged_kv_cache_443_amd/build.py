@@ -27,6 +27,7 @@ SOURCES = [
     "pa_reduce.hip",
     "pa_append.hip",
     "pa_copy.hip",
+    "pa_noalloc.hip",
     "pa_probe.hip",
     "pa_block_manager.cpp",
 ]

@@ -290,6 +290,37 @@ pa_status pa_reduce(const float *part_out, const float *part_lse, int32_t num_se
   return from_hip(pa::launch_reduce(p, stream));
 }
 
+pa_status pa_decode_split_noalloc(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads,
+                                  const pa_kv_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, float scale, int32_t partition_size, void *out,
+                                  pa_dtype out_dtype, hipStream_t stream) {
+  pa_status st = pa::check_decode_common(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq,
+                                         context_lens, scale);
+  if (st != PA_OK) return st;
+  if (partition_size < 1 || partition_size % cache->block_size != 0) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  st = pa::check_out(out, q_dtype, cache->kv_dtype, out_dtype);
+  if (st != PA_OK) return st;
+  // the fewest partitions that cover a table row; partials and lse must fit
+  // the library's scratch
+  const int64_t max_len = static_cast<int64_t>(max_blocks_per_seq) * cache->block_size;
+  const int32_t pmax = static_cast<int32_t>((max_len + partition_size - 1) / partition_size);
+  const size_t need = pa::split_workspace_bytes(num_seqs, num_heads, cache->head_dim, pmax);
+  if (need == 0 || need > pa::kNoAllocScratchBytes) return PA_ERR_BAD_WORKSPACE;
+  void *base = nullptr;
+  st = from_hip(pa::noalloc_scratch(&base));
+  if (st != PA_OK) return st;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * pmax;
+  const size_t lse_off = (rows * cache->head_dim * sizeof(float) + 255) / 256 * 256;
+  float *part_out = static_cast<float *>(base);
+  float *part_lse = reinterpret_cast<float *>(static_cast<unsigned char *>(base) + lse_off);
+  st = pa_decode_split(q, q_dtype, num_seqs, num_heads, cache, block_tables, max_blocks_per_seq, context_lens, scale,
+                       partition_size, pmax, part_out, part_lse, stream);
+  if (st != PA_OK) return st;
+  return pa_reduce(part_out, part_lse, num_seqs, num_heads, cache->head_dim, pmax, context_lens, partition_size, out,
+                   out_dtype, stream);
+}
+
 pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs,
                          hipStream_t stream) {
   pa_status st = pa::check_copy(cache, block_pairs, num_pairs);
@@ -322,7 +353,9 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
     case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or block_size combination";
     case PA_ERR_MISALIGNED: return "a pointer is not aligned as required";
-    case PA_ERR_BAD_WORKSPACE: return "max_num_partitions too small for max_blocks_per_seq * block_size";
+    case PA_ERR_BAD_WORKSPACE:
+      return "split scratch too small: max_num_partitions below ceil(max_blocks_per_seq * block_size / "
+             "partition_size), or partials beyond the fixed scratch of pa_decode_split_noalloc";
     case PA_ERR_HIP: return "HIP kernel launch failed (see pa_last_hip_error)";
     case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
     case PA_ERR_INVALID_BLOCK: return "a block id is out of range or not in use";

@@ -99,6 +99,14 @@ struct CopyParams {
 // pass indexes its sequences' pieces in LDS).
 constexpr int32_t kMaxFusedSplitSeqs = 4096;
 
+// Bytes of the library's own device scratch (pa_decode_split_noalloc): the
+// partials and log-sum-exps of one KV-split decode.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached; no allocation).
+hipError_t noalloc_scratch(void **ptr);
+
 // Launchers (one per kernel family); each returns the launch's hipError_t.
 hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);

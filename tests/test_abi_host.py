@@ -161,6 +161,23 @@ def test_split_rejections(L):
     assert _split(L, c, P=128, Pmax=4, B=0) == PA_OK  # no-op
 
 
+def _noalloc(L, cache, B=4, Hq=8, mbps=8, P=512, out=A16[7], odt=PA_F32):
+    return L.pa_decode_split_noalloc(A16[4], PA_BF16, B, Hq, ctypes.byref(cache), A16[5], mbps, A16[6], 0.1, P, out,
+                                     odt, None)
+
+
+def test_split_noalloc_rejections(L):
+    c = _cache(bs=64)
+    assert _noalloc(L, c, P=0) == PA_ERR_BAD_SHAPE
+    assert _noalloc(L, c, P=96) == PA_ERR_BAD_SHAPE  # not a multiple of block_size
+    assert _noalloc(L, c, out=None) == PA_ERR_NULL_PTR
+    assert _noalloc(L, c, out=A16[7] + 4) == PA_ERR_MISALIGNED
+    assert _noalloc(L, c, odt=PA_I8) == PA_ERR_UNSUPPORTED
+    # partials beyond the 32 MiB scratch: 64 seqs x 64 heads x 64 partitions x (128 + 1) floats
+    assert _noalloc(L, _cache(bs=64, H=8), B=64, Hq=64, mbps=512, P=512) == PA_ERR_BAD_WORKSPACE
+    assert _noalloc(L, c, B=0, out=None) == PA_OK  # no-op
+
+
 def _reduce(L, po=A16[8], pl=A16[9], B=4, Hq=8, D=128, Pmax=4, lens=A16[6], P=512, out=A16[7], odt=PA_BF16):
     return L.pa_reduce(po, pl, B, Hq, D, Pmax, lens, P, out, odt, None)
 
