@@ -193,9 +193,23 @@ def stats_us(v) -> dict:
             "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
 
 
-def _timed(torch, fn, steps: int, warmup: int, flush) -> list:
+SETTLE_S = 1.0
+
+
+def _timed(torch, fn, steps: int, warmup: int, flush, settle_s: float = SETTLE_S) -> list:
     """Durations (ms) of ``fn`` over ``steps`` calls, one event pair around each
-    call, the caches flushed before each."""
+    call, the caches flushed before each.  First the calls run untimed for at
+    least ``settle_s`` seconds and ``warmup`` calls: after seconds of host
+    work (filling a cache) the GPU's clocks have dropped, and the first calls
+    measured up to 20 % slower than a serving loop's steady state."""
+    t_end = time.perf_counter() + settle_s
+    while True:
+        for _ in range(8):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     for _ in range(warmup):
         flush()
         fn()
@@ -277,18 +291,7 @@ def time_copy_blocks(case: Case, steps: int, warmup: int, flush, max_pairs: int 
     rng = np.random.default_rng(5)
     pairs = np.stack([rng.choice(used, n, replace=False), rng.choice(free, n, replace=False)], axis=1)
     dev_pairs = torch.from_numpy(pairs.astype(np.int32)).to(case.q.device)
-    for _ in range(warmup):
-        flush()
-        pa.copy_blocks(case.cache, dev_pairs)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        flush()
-        a.record()
-        pa.copy_blocks(case.cache, dev_pairs)
-        b.record()
-    torch.cuda.synchronize()
-    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
+    us = stats_us(_timed(torch, lambda: pa.copy_blocks(case.cache, dev_pairs), steps, warmup, flush))["median_us"]
     s = case.s
     elem = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[s.kv_dtype]
     per_block = int(s.Hkv * s.bs * s.D * elem * 2) + (s.Hkv * s.bs * 2 * 2 if s.kv_dtype in ("i8", "i4") else 0)
@@ -314,18 +317,7 @@ def time_multi(case: Case, steps: int, warmup: int, flush, perfmodel, q_len: int
     def run():
         pa.decode_multi(qd, qs, q_len, case.cache, case.tables, case.lens, s.scale, out)
 
-    for _ in range(warmup):
-        flush()
-        run()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        flush()
-        a.record()
-        run()
-        b.record()
-    torch.cuda.synchronize()
-    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
+    us = stats_us(_timed(torch, run, steps, warmup, flush))["median_us"]
     nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=s.Hq, Hkv=s.Hkv, D=s.D, bs=s.bs,
                                    kv_dtype=s.kv_dtype, q_dtype=s.q_dtype,
                                    out_dtype="bf16" if case.out_dtype == torch.bfloat16 else "f32")
@@ -403,18 +395,7 @@ def time_multi_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flush
     def run():
         pa.decode_multi(qd, qs, n, cache, tables, lens, w.spec.scale, out)
 
-    for _ in range(warmup):
-        flush()
-        run()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        flush()
-        a.record()
-        run()
-        b.record()
-    torch.cuda.synchronize()
-    us = stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
+    us = stats_us(_timed(torch, run, steps, warmup, flush))["median_us"]
     nbytes = perfmodel.multi_bytes(w.context_lens, counts, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype="bf16",
                                    q_dtype="bf16", out_dtype="bf16")
     flops = perfmodel.multi_flops(w.context_lens, counts, Hq=Hq, D=128)
@@ -461,18 +442,7 @@ def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flus
         pa.reduce(po, pl, lens, P, out)
 
     def timed(run):
-        for _ in range(warmup):
-            flush()
-            run()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in ev:
-            flush()
-            a.record()
-            run()
-            b.record()
-        torch.cuda.synchronize()
-        return stats_us([a.elapsed_time(b) for a, b in ev])["median_us"]
+        return stats_us(_timed(torch, run, steps, warmup, flush))["median_us"]
 
     us, us_split = timed(single), timed(split)
     nbytes = perfmodel.decode_bytes(w.context_lens, Hq=Hq, Hkv=Hkv, D=128, bs=16, kv_dtype=kv, q_dtype="bf16",
