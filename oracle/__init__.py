@@ -40,6 +40,12 @@ another precision):
   PagedAttention question, scheduling list; page "vLLM框架是怎么做推理加速的",
   section 2 and its second follow-up).
 
+* ``mla_decode`` / ``mla_append``: decode over an MLA latent cache -- one
+  compressed vector per token, each head's K and V recovered by the
+  up-projections K = c W_up_K, V = c W_up_V, then attended as in
+  ``decode`` (page "字节跳动 AI Infra (2)", question on KV-cache principles,
+  MLA paragraph).  Pinned by ``tests/test_oracle_mla.py``.
+
 Parity status: every function here is pinned by tests that do not re-use
 its own code path (closed forms, invariants, pure-Python brute force, the
 pages' worked block counts); see ``tests/test_oracle_pins.py``.
@@ -59,3 +65,4 @@ from .paged import (  # noqa: F401
 )
 from .brute import decode_bruteforce  # noqa: F401
 from .blocks import BlockManager, OutOfBlocks, copy_blocks, swap_blocks  # noqa: F401
+from .mla import LatentCache, mla_append, mla_build_cache, mla_decode, mla_expand, mla_gather  # noqa: F401,E402

@@ -10,7 +10,8 @@ The five workloads follow the decode batches described for the method:
 a tiny MHA case, a LLaMA-13B-shaped MHA layer, a 70B-shaped GQA layer with
 chat-like length spread and beam pairs that share prefix blocks
 (copy-on-write), a long-context GQA case for the KV-split path and an int8
-KV-cache GQA case with cache append.
+KV-cache GQA case with cache append; ``workloads.mla`` draws decode batches
+over an MLA latent cache.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
@@ -23,3 +24,4 @@ from .gen import (  # noqa: F401
     bf16_from_bits,
     blocks_needed,
 )
+from .mla import MLA_CONFIG, MlaSpec, MlaWorkload, make_mla, make_mla_custom  # noqa: F401,E402
