@@ -68,6 +68,7 @@ def parse_args(argv=None):
                     help="upper bound on the oracle's timed CPU work")
     ap.add_argument("--no-multi-shapes", action="store_true",
                     help="skip the extra multi-query shapes (verification and chunked-prefill sizes)")
+    ap.add_argument("--no-mla", action="store_true", help="skip the MLA latent-cache decode")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (calibrates rocprofv3 byte counters)")
@@ -455,6 +456,43 @@ def time_decode_shape(torch, pa, perfmodel, shape, steps: int, warmup: int, flus
             "split_512_plus_merge_us": round(us_split, 2), "split_frac_of_hbm_peak": frac(us_split)}
 
 
+def time_mla(torch, pa, perfmodel, steps: int, warmup: int, flush) -> dict:
+    """pa_mla_decode on the MLA latent-cache batch (128 sequences of 1024-8192
+    tokens, 16 heads of 128 over a 512-wide latent, bf16): one call = query
+    absorption, the attention pass over the latent cache, merge and output
+    projection.  Algorithmic bytes: every cached latent row once, the two
+    up-projections, q, out and the tables."""
+    from workloads import make_mla
+    from workloads.device import mla_fill, mla_to_dev
+
+    w = make_mla()
+    s = w.spec
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    cache = mla_fill(w, dev)
+    torch.cuda.synchronize()
+    log(f"mla: {s.name} B={w.B} tokens={w.total_tokens()} latent cache filled in {time.time() - t0:.1f}s")
+    q, wk, wv = mla_to_dev(w.q, dev), mla_to_dev(w.w_uk, dev), mla_to_dev(w.w_uv, dev)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    P = s.partition_size
+    ws = torch.empty(pa.mla_workspace_bytes(w.B, s.H, cache, tables.shape[1], P), dtype=torch.uint8, device=dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    t = stats_us(_timed(torch, lambda: pa.mla_decode(q, wk, wv, cache, tables, lens, s.scale, P, ws, out), steps,
+                        warmup, flush))
+    nbytes = perfmodel.mla_bytes(w.context_lens, H=s.H, d_h=s.d_h, d_c=s.d_c, bs=s.bs)
+    flops = perfmodel.mla_flops(w.context_lens, H=s.H, d_h=s.d_h, d_c=s.d_c)
+    us = t["median_us"]
+    del cache, ws, out, q, wk, wv
+    torch.cuda.empty_cache()
+    return {"workload": s.name, "batch": w.B, "q_heads": s.H, "head_dim": s.d_h, "latent_dim": s.d_c,
+            "block_size": s.bs, "partition_size": P, "cached_tokens": w.total_tokens(),
+            "us": round(us, 2), "us_stats": {k: round(v, 2) for k, v in t.items()}, "bytes": nbytes,
+            "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / perfmodel.HBM_PEAK_GBPS, 4),
+            "TFLOPs": round(flops / us / 1e6, 1),
+            "frac_of_mfma_peak": round(flops / us / 1e6 / perfmodel.MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def summarise(case: Case, t: dict, peak: float, probe: dict) -> dict:
     """A workload's line: the step (median and spread), every kernel timed
     alone, and the roofline block of the step's dominant kernel."""
@@ -727,6 +765,9 @@ def main(argv=None) -> int:
             mqa[shape[0]] = time_decode_shape(torch, pa, perfmodel, shape, args.steps, args.warmup, flush)
             log(f"decode {shape[0]}: {mqa[shape[0]]}")
         line["decode_mqa"] = mqa
+    if not args.no_mla:
+        line["mla_decode"] = time_mla(torch, pa, perfmodel, args.steps, args.warmup, flush)
+        log(f"mla_decode: {line['mla_decode']}")
 
     other = {}
     extra = [(c, {}) for c in others]

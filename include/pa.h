@@ -356,6 +356,76 @@ pa_status pa_swap_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const i
                          int32_t num_pairs, hipStream_t stream);
 
 /*
+ * MLA latent cache -- multi-head latent attention (page "字节跳动 AI Infra
+ * (2)", question on KV-cache principles, the MLA paragraph and the MLA row
+ * of its optimisation table).  Each token's K and V are compressed jointly
+ * into one latent row c (latent_dim wide, 512 in the page's example); the
+ * cache stores only c, and the heads' keys and values are recovered by the
+ * up-projections K = c W_uk and V = c W_uv (latent_dim -> num_heads x
+ * head_dim; head h is column block h, channel d of head h is column
+ * h * head_dim + d).  The V projection is this library's reading: the page
+ * writes out the K one and says K and V are compressed together.
+ *
+ * Layout: latent [num_blocks][block_size][latent_dim] bf16, the row of
+ * logical position t of a sequence in block block_tables[b][t / block_size]
+ * at offset t % block_size.  Pointers are device pointers.
+ */
+typedef struct pa_latent_cache {
+  void *latent;         /* bf16, 16-byte aligned */
+  int32_t num_blocks;   /* >= 1 */
+  int32_t block_size;   /* 16, 32 or 64 */
+  int32_t latent_dim;   /* 512 */
+} pa_latent_cache;
+
+/*
+ * pa_mla_append -- write new tokens' latent rows into their slots.
+ *
+ *   latent_rows   bf16 [num_tokens][latent_dim], 16-byte aligned
+ *   slot_mapping  int32 [num_tokens]: row i goes to block s / block_size,
+ *                 offset s % block_size; s < 0 or s >= num_blocks *
+ *                 block_size skips it.  Bit-exact copy.
+ * num_tokens == 0 is a no-op.  Preconditions (device data): slots distinct.
+ */
+pa_status pa_mla_append(const void *latent_rows, const int32_t *slot_mapping, int32_t num_tokens,
+                        const pa_latent_cache *cache, hipStream_t stream);
+
+/* Workspace bytes of pa_mla_decode (absorbed queries, partial outputs and
+ * log-sum-exps); 0 on invalid sizes. */
+size_t pa_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t latent_dim, int32_t max_blocks_per_seq,
+                              int32_t block_size, int32_t partition_size);
+
+/*
+ * pa_mla_decode -- decode attention over an MLA latent cache.
+ *
+ * For sequence b with L = context_lens[b] cached tokens and query head h:
+ *     K_t = c_t W_uk[:, h],  V_t = c_t W_uv[:, h],
+ *     out[b][h] = sum_{t < L} softmax_t(scale * q[b][h] . K_t) V_t;
+ * L == 0 gives a zero row.  Computed without forming K or V: the query is
+ * moved into the latent space (q_lat = W_uk[:, h] q), attention runs over
+ * the latent rows in partitions of partition_size tokens (normalised
+ * partial latent outputs and log-sum-exps, merged as pa_reduce merges), and
+ * the merged latent output is projected by W_uv[:, h].  fp32 accumulation;
+ * bf16 out is the round-to-nearest-even of the fp32 result.
+ *
+ *   q               bf16 [num_seqs][num_heads][head_dim], 16-byte aligned
+ *   head_dim        64 or 128;  num_heads >= 1;  num_seqs <= 4096
+ *   w_uk, w_uv      bf16 [latent_dim][num_heads * head_dim], 16-byte aligned
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq] (whole row readable)
+ *   context_lens    int32 [num_seqs]
+ *   partition_size  a multiple of 64 and of block_size, at most 4096
+ *   workspace       device memory, 256-byte aligned, workspace_bytes >=
+ *                   pa_mla_workspace_bytes(...) (else PA_ERR_BAD_WORKSPACE)
+ *   out             [num_seqs][num_heads][head_dim], out_dtype PA_F32 or PA_BF16
+ * Preconditions (device data): 0 <= L <= max_blocks_per_seq * block_size;
+ * the first ceil(L / block_size) entries of each row are < num_blocks.
+ * num_seqs == 0 is a no-op.
+ */
+pa_status pa_mla_decode(const void *q, int32_t num_seqs, int32_t num_heads, int32_t head_dim, const void *w_uk,
+                        const void *w_uv, const pa_latent_cache *cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, float scale, int32_t partition_size,
+                        void *workspace, size_t workspace_bytes, void *out, pa_dtype out_dtype, hipStream_t stream);
+
+/*
  * Block manager -- host bookkeeping of a block pool (no GPU work).
  *
  * Reference counts of num_blocks physical blocks of block_size tokens.  Blocks

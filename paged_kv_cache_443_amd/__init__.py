@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PA_BF16, PA_F32, PA_I4, PA_I8, PaKvCache
+from ._lib import PA_BF16, PA_F32, PA_I4, PA_I8, PaKvCache, PaLatentCache
 
 __all__ = [
     "PAError",
@@ -31,6 +31,10 @@ __all__ = [
     "reduce",
     "split_workspace_bytes",
     "probe_read",
+    "LatentCache",
+    "mla_append",
+    "mla_workspace_bytes",
+    "mla_decode",
     "max_partitions",
     "copy_blocks",
     "swap_blocks",
@@ -301,6 +305,66 @@ def reduce(part_out: torch.Tensor, part_lse: torch.Tensor, context_lens: torch.T
     st = _lib.lib().pa_reduce(_ptr(part_out), _ptr(part_lse), B, Hq, D, Pmax, _ptr(context_lens), int(partition_size),
                               _ptr(out), _DT[out.dtype], _stream(out.device))
     _check("pa_reduce", st)
+    return out
+
+
+@dataclass
+class LatentCache:
+    """One layer's paged MLA latent cache: ``latent`` bf16 ``[num_blocks, block_size, latent_dim]``."""
+
+    latent: torch.Tensor
+    num_blocks: int
+    block_size: int
+    latent_dim: int
+
+    @classmethod
+    def allocate(cls, num_blocks: int, block_size: int, latent_dim: int = 512, device="cuda") -> "LatentCache":
+        t = torch.empty((num_blocks, block_size, latent_dim), dtype=torch.bfloat16, device=device)
+        return cls(t, num_blocks, block_size, latent_dim)
+
+    def descriptor(self) -> PaLatentCache:
+        _need(self.latent, "latent", torch.bfloat16, (self.num_blocks, self.block_size, self.latent_dim))
+        return PaLatentCache(_ptr(self.latent), self.num_blocks, self.block_size, self.latent_dim)
+
+
+def mla_append(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: LatentCache) -> None:
+    """Write latent rows ``[T, latent_dim]`` (bf16) into slots ``slot_mapping[T]`` (int32, -1 skips)."""
+    T = rows.shape[0]
+    _need(rows, "rows", torch.bfloat16, (T, cache.latent_dim))
+    _need(slot_mapping, "slot_mapping", torch.int32, (T,))
+    desc = cache.descriptor()
+    _check("pa_mla_append", _lib.lib().pa_mla_append(_ptr(rows), _ptr(slot_mapping), T, ctypes.byref(desc),
+                                                     _stream(rows.device)))
+
+
+def mla_workspace_bytes(num_seqs: int, num_heads: int, cache: LatentCache, max_blocks_per_seq: int,
+                        partition_size: int) -> int:
+    return int(_lib.lib().pa_mla_workspace_bytes(num_seqs, num_heads, cache.latent_dim, max_blocks_per_seq,
+                                                 cache.block_size, partition_size))
+
+
+def mla_decode(q: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, cache: LatentCache,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, partition_size: int,
+               workspace: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """Decode over an MLA latent cache: ``q`` bf16 ``[B, H, head_dim]``, up-projections ``w_uk`` / ``w_uv``
+    bf16 ``[latent_dim, H * head_dim]``, a device ``workspace`` of at least ``mla_workspace_bytes`` bytes;
+    writes and returns ``out`` ``[B, H, head_dim]`` (fp32 or bf16)."""
+    B, H, D = q.shape
+    _need(q, "q", torch.bfloat16)
+    _need(w_uk, "w_uk", torch.bfloat16, (cache.latent_dim, H * D))
+    _need(w_uv, "w_uv", torch.bfloat16, (cache.latent_dim, H * D))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(workspace, "workspace")
+    _need(out, "out", (torch.float32, torch.bfloat16), (B, H, D))
+    desc = cache.descriptor()
+    st = _lib.lib().pa_mla_decode(_ptr(q), B, H, D, _ptr(w_uk), _ptr(w_uv), ctypes.byref(desc), _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(context_lens), float(scale), int(partition_size),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                  _DT[out.dtype], _stream(q.device))
+    _check("pa_mla_decode", st)
     return out
 
 

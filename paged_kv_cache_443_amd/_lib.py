@@ -45,6 +45,9 @@ EXPORTED = (
     "pa_bm_append_slot",
     "pa_split_workspace_bytes",
     "pa_probe_read",
+    "pa_mla_append",
+    "pa_mla_workspace_bytes",
+    "pa_mla_decode",
     "pa_status_string",
     "pa_last_hip_error",
 )
@@ -63,6 +66,17 @@ class PaKvCache(ctypes.Structure):
         ("block_size", c_int32),
         ("head_dim", c_int32),
         ("kv_dtype", c_int),
+    ]
+
+
+class PaLatentCache(ctypes.Structure):
+    """Mirror of ``pa_latent_cache``."""
+
+    _fields_ = [
+        ("latent", c_void_p),
+        ("num_blocks", c_int32),
+        ("block_size", c_int32),
+        ("latent_dim", c_int32),
     ]
 
 
@@ -128,6 +142,14 @@ def lib() -> ctypes.CDLL:
     L.pa_split_workspace_bytes.restype = c_size_t
     L.pa_probe_read.argtypes = [c_void_p, c_size_t, c_int32, c_int32, c_void_p, c_void_p]
     L.pa_probe_read.restype = c_int
+    LP = ctypes.POINTER(PaLatentCache)
+    L.pa_mla_append.argtypes = [c_void_p, c_void_p, c_int32, LP, c_void_p]
+    L.pa_mla_append.restype = c_int
+    L.pa_mla_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]
+    L.pa_mla_workspace_bytes.restype = c_size_t
+    L.pa_mla_decode.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, LP, c_void_p, c_int32,
+                                c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p, c_int, c_void_p]
+    L.pa_mla_decode.restype = c_int
     L.pa_status_string.argtypes = [c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_hip_error.argtypes = []

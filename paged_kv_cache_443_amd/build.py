@@ -29,6 +29,7 @@ SOURCES = [
     "pa_copy.hip",
     "pa_noalloc.hip",
     "pa_probe.hip",
+    "pa_mla.hip",
     "pa_block_manager.cpp",
 ]
 

@@ -321,6 +321,61 @@ pa_status pa_decode_split_noalloc(const void *q, pa_dtype q_dtype, int32_t num_s
                    out_dtype, stream);
 }
 
+pa_status pa_mla_append(const void *latent_rows, const int32_t *slot_mapping, int32_t num_tokens,
+                        const pa_latent_cache *cache, hipStream_t stream) {
+  const pa_status st = pa::check_mla_append(latent_rows, slot_mapping, num_tokens, cache);
+  if (st != PA_OK || num_tokens == 0) return st;
+  pa::MlaAppendParams p{};
+  p.rows = static_cast<const uint16_t *>(latent_rows);
+  p.slot_mapping = slot_mapping;
+  p.cache = static_cast<uint16_t *>(cache->latent);
+  p.num_tokens = num_tokens;
+  p.num_blocks = cache->num_blocks;
+  p.block_size = cache->block_size;
+  return from_hip(pa::launch_mla_append(p, stream));
+}
+
+size_t pa_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t latent_dim, int32_t max_blocks_per_seq,
+                              int32_t block_size, int32_t partition_size) {
+  return pa::mla_workspace(num_seqs, num_heads, latent_dim, max_blocks_per_seq, block_size, partition_size).total;
+}
+
+pa_status pa_mla_decode(const void *q, int32_t num_seqs, int32_t num_heads, int32_t head_dim, const void *w_uk,
+                        const void *w_uv, const pa_latent_cache *cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, float scale, int32_t partition_size,
+                        void *workspace, size_t workspace_bytes, void *out, pa_dtype out_dtype, hipStream_t stream) {
+  const pa_status st = pa::check_mla_decode(q, num_seqs, num_heads, head_dim, w_uk, w_uv, cache, block_tables,
+                                            max_blocks_per_seq, context_lens, scale, partition_size, workspace,
+                                            workspace_bytes, out, out_dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  const pa::MlaWorkspace ws = pa::mla_workspace(num_seqs, num_heads, cache->latent_dim, max_blocks_per_seq,
+                                                cache->block_size, partition_size);
+  unsigned char *base = static_cast<unsigned char *>(workspace);
+  pa::MlaParams p{};
+  p.q = static_cast<const uint16_t *>(q);
+  p.w_uk = static_cast<const uint16_t *>(w_uk);
+  p.w_uv = static_cast<const uint16_t *>(w_uv);
+  p.cache = static_cast<const uint16_t *>(cache->latent);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.q_lat = reinterpret_cast<float *>(base);
+  p.part_out = reinterpret_cast<float *>(base + ws.part_out_off);
+  p.part_lse = reinterpret_cast<float *>(base + ws.part_lse_off);
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.head_dim = head_dim;
+  p.block_size = cache->block_size;
+  p.num_blocks = cache->num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.partition_size = partition_size;
+  p.max_num_partitions = ws.max_num_partitions;
+  p.head_groups = (num_heads + 15) / 16;
+  p.scale_log2 = scale * kLog2e;
+  p.out_bf16 = out_dtype == PA_BF16;
+  return from_hip(pa::launch_mla_decode(p, stream));
+}
+
 pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *block_pairs, int32_t num_pairs,
                          hipStream_t stream) {
   pa_status st = pa::check_copy(cache, block_pairs, num_pairs);

@@ -34,6 +34,14 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
 // from every 8 tokens sit side by side (one 128-byte line per load).
 __host__ __device__ __forceinline__ int bf16_k_slot(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
+// Work-group barrier for LDS hand-offs inside a streaming loop.  It waits for
+// this wavefront's LDS operations only (lgkmcnt) before s_barrier, not for
+// its global loads still in flight, which __syncthreads() (a work-group
+// fence) would drain: a prefetch issued before the barrier stays in flight
+// across it.  The memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 2^x on the transcendental unit (inputs here are <= 0 or -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -95,6 +95,49 @@ struct CopyParams {
   size_t tile_bytes;          // one (block, kv head) tile of one pool
 };
 
+// MLA decode over a paged latent cache (pa_mla_decode).
+struct MlaParams {
+  const uint16_t *q;          // [B][H][head_dim] bf16
+  const uint16_t *w_uk;       // [latent_dim][H * head_dim] bf16: K = c W_uk
+  const uint16_t *w_uv;       // [latent_dim][H * head_dim] bf16: V = c W_uv
+  const uint16_t *cache;      // [num_blocks][block_size][latent_dim] bf16
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *q_lat;               // workspace: [B][H][latent_dim] absorbed queries
+  float *part_out;            // workspace: [B][H][Pmax][latent_dim] normalised partial latent outputs
+  float *part_lse;            // workspace: [B][H][Pmax]
+  void *out;                  // [B][H][head_dim]
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t partition_size;
+  int32_t max_num_partitions;
+  int32_t head_groups;        // ceil(H / 16)
+  float scale_log2;           // scale * log2(e)
+  int32_t out_bf16;
+};
+
+// Latent rows written into their slots (pa_mla_append).
+struct MlaAppendParams {
+  const uint16_t *rows;       // [T][latent_dim] bf16
+  const int32_t *slot_mapping;
+  uint16_t *cache;
+  int32_t num_tokens;
+  int32_t num_blocks;
+  int32_t block_size;
+};
+
+// Latent width the MLA kernels are built for (the pages' 512).
+constexpr int32_t kMlaLatentDim = 512;
+// Tokens per MLA chunk; partitions are a multiple of it.
+constexpr int32_t kMlaChunk = 64;
+// Largest MLA partition and batch (the persistent pass indexes pieces in LDS).
+constexpr int32_t kMlaMaxPartition = 4096;
+constexpr int32_t kMlaMaxSeqs = 4096;
+
 // Largest batch the fused append + split pass takes (the persistent split
 // pass indexes its sequences' pieces in LDS).
 constexpr int32_t kMaxFusedSplitSeqs = 4096;
@@ -113,6 +156,8 @@ hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);
+hipError_t launch_mla_decode(const MlaParams &p, hipStream_t s);
+hipError_t launch_mla_append(const MlaAppendParams &p, hipStream_t s);
 hipError_t launch_probe_read(const void *buf, size_t bytes, int mode, int tile_bytes, uint32_t *sink, hipStream_t s);
 
 }  // namespace pa

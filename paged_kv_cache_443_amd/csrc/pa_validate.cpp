@@ -160,6 +160,76 @@ pa_status check_probe(const void *buf, size_t bytes, int32_t mode, int32_t tile_
   return PA_OK;
 }
 
+pa_status check_latent_cache(const pa_latent_cache *c) {
+  if (c == nullptr || c->latent == nullptr) return PA_ERR_NULL_PTR;
+  if (c->num_blocks < 1 || c->block_size < 1 || c->latent_dim < 1) return PA_ERR_BAD_SHAPE;
+  if (!supported_block_size(c->block_size) || c->latent_dim != 512) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(c->num_blocks) * c->block_size > INT32_MAX) return PA_ERR_BAD_SHAPE;  // int32 slots
+  if (!aligned(c->latent, 16)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+pa_status check_mla_append(const void *rows, const int32_t *slot_mapping, int32_t num_tokens,
+                           const pa_latent_cache *cache) {
+  pa_status st = check_latent_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (rows == nullptr || slot_mapping == nullptr) return PA_ERR_NULL_PTR;
+  if (!aligned(rows, 16) || !aligned(slot_mapping, 4)) return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
+MlaWorkspace mla_workspace(int32_t num_seqs, int32_t num_heads, int32_t latent_dim, int32_t max_blocks_per_seq,
+                           int32_t block_size, int32_t partition_size) {
+  MlaWorkspace w{0, 0, 0, 0};
+  if (num_seqs < 0 || num_heads < 1 || latent_dim < 1 || max_blocks_per_seq < 1 || block_size < 1 ||
+      partition_size < 1)
+    return w;
+  const int64_t max_len = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t pmax = (max_len + partition_size - 1) / partition_size;
+  if (pmax > INT32_MAX) return w;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  const size_t qlat = rows * latent_dim * sizeof(float);
+  w.part_out_off = (qlat + 255) / 256 * 256;
+  const size_t po = rows * static_cast<size_t>(pmax) * latent_dim * sizeof(float);
+  w.part_lse_off = (w.part_out_off + po + 255) / 256 * 256;
+  w.total = w.part_lse_off + rows * static_cast<size_t>(pmax) * sizeof(float);
+  w.max_num_partitions = static_cast<int32_t>(pmax);
+  return w;
+}
+
+pa_status check_mla_decode(const void *q, int32_t num_seqs, int32_t num_heads, int32_t head_dim, const void *w_uk,
+                           const void *w_uv, const pa_latent_cache *cache, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens, float scale,
+                           int32_t partition_size, const void *workspace, size_t workspace_bytes, const void *out,
+                           pa_dtype out_dtype) {
+  pa_status st = check_latent_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if (num_seqs > 4096) return PA_ERR_BAD_SHAPE;  // the persistent pass indexes its pieces in LDS
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * cache->block_size > INT32_MAX) return PA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(num_heads) * head_dim > INT32_MAX / 512) return PA_ERR_BAD_SHAPE;
+  if (partition_size < 64 || partition_size % 64 != 0 || partition_size % cache->block_size != 0 ||
+      partition_size > 4096)
+    return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (q == nullptr || w_uk == nullptr || w_uv == nullptr || block_tables == nullptr || context_lens == nullptr ||
+      workspace == nullptr || out == nullptr)
+    return PA_ERR_NULL_PTR;
+  if (raw(out_dtype) != PA_F32 && raw(out_dtype) != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const MlaWorkspace ws = mla_workspace(num_seqs, num_heads, cache->latent_dim, max_blocks_per_seq,
+                                        cache->block_size, partition_size);
+  if (ws.total == 0) return PA_ERR_BAD_SHAPE;
+  if (workspace_bytes < ws.total) return PA_ERR_BAD_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 256))
+    return PA_ERR_MISALIGNED;
+  return PA_OK;
+}
+
 size_t split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_num_partitions) {
   if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_num_partitions < 1) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * max_num_partitions;

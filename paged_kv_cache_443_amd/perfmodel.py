@@ -89,3 +89,25 @@ def append_bytes(num_tokens: int, *, Hkv: int, D: int, kv_dtype: str, src_dtype:
 def split_scratch_bytes(B: int, Hq: int, D: int, num_partitions_used: int) -> int:
     """Partial outputs and LSEs written by the split pass and read by the merge (overhead)."""
     return int(2 * num_partitions_used * (D + 1) * 4 * Hq) if B else 0
+
+
+def mla_bytes(context_lens: Iterable[int], *, H: int, d_h: int, d_c: int, bs: int) -> int:
+    """Bytes one MLA decode over a latent cache must move: the latent row (bf16)
+    of every cached token once, the two bf16 up-projections, q read and out
+    written (bf16), the used block-table entries and the context lengths.
+    The workspace (absorbed queries, partials) is overhead and not counted."""
+    L = np.asarray(list(context_lens), dtype=np.int64)
+    B = len(L)
+    latent = int(L.sum()) * d_c * 2
+    weights = 2 * d_c * H * d_h * 2
+    qo = B * H * d_h * 2 * 2
+    tables = int(np.sum((L + bs - 1) // bs)) * 4 + B * 4
+    return int(latent + weights + qo + tables)
+
+
+def mla_flops(context_lens: Iterable[int], *, H: int, d_h: int, d_c: int) -> int:
+    """Algorithmic flops of MLA decode in the absorbed form: per cached token and
+    head a d_c-wide score and a d_c-wide weighted sum (4 d_c), plus the query
+    absorption and the output projection (2 d_c d_h each) per (sequence, head)."""
+    L = np.asarray(list(context_lens), dtype=np.int64)
+    return int(int(L.sum()) * H * 4 * d_c + len(L) * H * 4 * d_c * d_h)

@@ -17,6 +17,8 @@ hipError_t launch_decode_f32(const DecodeParams &, int, int, hipStream_t) { retu
 hipError_t launch_reduce(const ReduceParams &, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_append(const AppendParams &, pa_dtype, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_copy_blocks(const CopyParams &, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_mla_decode(const MlaParams &, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_mla_append(const MlaAppendParams &, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_probe_read(const void *, size_t, int, int, uint32_t *, hipStream_t) { return hipErrorNoDevice; }
 hipError_t noalloc_scratch(void **ptr) {
   *ptr = nullptr;

@@ -9,7 +9,8 @@ import pytest
 
 from paged_kv_cache_443_amd import _lib
 from paged_kv_cache_443_amd._lib import (PA_BF16, PA_ERR_BAD_SHAPE, PA_ERR_BAD_WORKSPACE, PA_ERR_MISALIGNED,
-                                         PA_ERR_NULL_PTR, PA_ERR_UNSUPPORTED, PA_F32, PA_I4, PA_I8, PA_OK, PaKvCache)
+                                         PA_ERR_NULL_PTR, PA_ERR_UNSUPPORTED, PA_F32, PA_I4, PA_I8, PA_OK, PaKvCache,
+                                         PaLatentCache)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
@@ -243,3 +244,43 @@ def test_probe_rejections(L):
     assert probe(mode=2, tile=2 << 20) == PA_ERR_BAD_SHAPE  # a tile larger than the buffer
     assert probe(buf=A16[0] + 8) == PA_ERR_MISALIGNED
     assert probe(snk=sink + 2) == PA_ERR_MISALIGNED
+
+
+def test_mla_rejections(L):
+    def lc(nb=64, bs=16, dc=512, ptr=A16[0]):
+        return PaLatentCache(ptr, nb, bs, dc)
+
+    def dec(cache=None, q=A16[4], B=4, H=16, D=128, wk=A16[1], wv=A16[2], tables=A16[5], mbps=8, lens=A16[6],
+            scale=0.1, P=1024, ws=A16[8], wsb=1 << 24, out=A16[7], odt=PA_BF16):
+        c = cache if cache is not None else lc()
+        return L.pa_mla_decode(q, B, H, D, wk, wv, ctypes.byref(c), tables, mbps, lens, scale, P, ws, wsb, out, odt,
+                               None)
+
+    need = L.pa_mla_workspace_bytes(4, 16, 512, 8, 16, 1024)
+    assert need == 4 * 16 * 512 * 4 + 4 * 16 * 1 * 512 * 4 + 256  # q_lat, one partition of partials, lse padded
+    assert dec(q=None) == PA_ERR_NULL_PTR
+    assert dec(wk=None) == PA_ERR_NULL_PTR
+    assert dec(ws=None) == PA_ERR_NULL_PTR
+    assert dec(cache=lc(ptr=None)) == PA_ERR_NULL_PTR
+    assert dec(cache=lc(dc=256)) == PA_ERR_UNSUPPORTED
+    assert dec(cache=lc(bs=8)) == PA_ERR_UNSUPPORTED
+    assert dec(cache=lc(nb=0)) == PA_ERR_BAD_SHAPE
+    assert dec(D=96) == PA_ERR_UNSUPPORTED
+    assert dec(H=0) == PA_ERR_BAD_SHAPE
+    assert dec(B=4097) == PA_ERR_BAD_SHAPE
+    assert dec(P=96) == PA_ERR_BAD_SHAPE       # not a multiple of 64
+    assert dec(P=8192) == PA_ERR_BAD_SHAPE     # longer than 4096
+    assert dec(cache=lc(bs=64), P=96) == PA_ERR_BAD_SHAPE  # not a multiple of the block size either
+    assert dec(scale=float("inf")) == PA_ERR_BAD_SHAPE
+    assert dec(wsb=need - 1) == PA_ERR_BAD_WORKSPACE
+    assert dec(odt=PA_I8) == PA_ERR_UNSUPPORTED
+    assert dec(ws=A16[8] + 16) == PA_ERR_MISALIGNED  # workspace must be 256-byte aligned
+    assert dec(q=A16[4] + 8) == PA_ERR_MISALIGNED
+    assert dec(B=0, q=None, out=None, ws=None) == PA_OK  # no-op
+    app = lambda rows=A16[9], slots=A16[10], T=3, cache=None: L.pa_mla_append(  # noqa: E731
+        rows, slots, T, ctypes.byref(cache if cache is not None else lc()), None)
+    assert app(rows=None) == PA_ERR_NULL_PTR
+    assert app(T=-1) == PA_ERR_BAD_SHAPE
+    assert app(slots=A16[10] + 2) == PA_ERR_MISALIGNED
+    assert app(cache=lc(dc=128)) == PA_ERR_UNSUPPORTED
+    assert app(T=0, rows=None, slots=None) == PA_OK

@@ -105,3 +105,20 @@ def new_token_batch(w, device: str = DEV) -> Tuple[torch.Tensor, torch.Tensor, t
     Kn, Vn, sl = w.new_tokens()
     sd = src_dtype(w.spec.kv_dtype)
     return to_dev_values(Kn, sd, device), to_dev_values(Vn, sd, device), torch.from_numpy(sl).to(device)
+
+
+def mla_to_dev(x: np.ndarray, device: str = DEV) -> torch.Tensor:
+    """float32 values (exact in bf16) -> bf16 device tensor."""
+    return to_dev_values(x, "bf16", device)
+
+
+def mla_fill(w, device: str = DEV) -> "pa.LatentCache":
+    """Device latent pool of an ``MlaWorkload``, every element NaN, then every
+    cached token written by ``pa_mla_append``."""
+    s = w.spec
+    c = pa.LatentCache.allocate(w.num_blocks, s.bs, s.d_c, device)
+    c.latent.view(torch.int16).fill_(0x7FC0)
+    for b in range(s.B):
+        if int(w.context_lens[b]):
+            pa.mla_append(mla_to_dev(w.latent(b), device), torch.from_numpy(w.slots(b)).to(device), c)
+    return c
