@@ -69,6 +69,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-multi-shapes", action="store_true",
                     help="skip the extra multi-query shapes (verification and chunked-prefill sizes)")
     ap.add_argument("--no-mla", action="store_true", help="skip the MLA latent-cache decode")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds each timed call runs untimed first, so the GPU clocks settle (0 for profiler runs)")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (calibrates rocprofv3 byte counters)")
@@ -194,16 +196,16 @@ def stats_us(v) -> dict:
             "p10_us": 1e3 * v[len(v) // 10], "p90_us": 1e3 * v[(9 * len(v)) // 10]}
 
 
-SETTLE_S = 1.0
+SETTLE_S = 1.0  # set from --settle-s
 
 
-def _timed(torch, fn, steps: int, warmup: int, flush, settle_s: float = SETTLE_S) -> list:
+def _timed(torch, fn, steps: int, warmup: int, flush, settle_s=None) -> list:
     """Durations (ms) of ``fn`` over ``steps`` calls, one event pair around each
     call, the caches flushed before each.  First the calls run untimed for at
     least ``settle_s`` seconds and ``warmup`` calls: after seconds of host
     work (filling a cache) the GPU's clocks have dropped, and the first calls
     measured up to 20 % slower than a serving loop's steady state."""
-    t_end = time.perf_counter() + settle_s
+    t_end = time.perf_counter() + (SETTLE_S if settle_s is None else settle_s)
     while True:
         for _ in range(8):
             flush()
@@ -656,6 +658,8 @@ def cpu_baseline(case: Case, budget_s: float, perfmodel, gpu_out_f32, min_s: flo
 
 def main(argv=None) -> int:
     args = parse_args(argv)
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle_s)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged-decode path has no "

@@ -121,28 +121,6 @@ def test_int4_decode_and_split_match_oracle(case):
             assert np.max(np.abs(gl[b, :, :n] - want_pl[b, :, :n])) <= 1e-3
 
 
-def test_int4_full_size_workload_sampled():
-    """The int8 workload's shape at full size with an int4 cache written by the
-    GPU append (256 sequences, up to 8192 tokens); sampled sequences against
-    the oracle."""
-    w = make_workload(5, kv_dtype="i4")
-    s = w.spec
-    say(f"[int4 full] B={w.B} tokens={w.total_tokens()} pool={w.num_blocks}")
-    cache = poisoned_cache(w)
-    gpu_append_tokens(w, cache)
-    q, tables, lens = meta(w)
-    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
-    pa.decode(q, cache, tables, lens, s.scale, out)
-    torch.cuda.synchronize()
-    assert torch.all(torch.isfinite(out))
-    picks = sorted({0, int(np.argmax(w.context_lens)), w.B // 2, w.B - 1})
-    oc = oracle.build_cache(w, seqs=picks)
-    want = oracle.decode(w.q[picks], oc, w.block_tables[picks], w.context_lens[picks], s.scale)
-    err = max_err(out[picks], want)
-    say(f"  sampled seqs {picks}: max abs err {err:.3e}")
-    assert err <= TOL["i4"]
-
-
 def test_int4_multi_query_matches_oracle():
     w = make_custom(B=5, Hq=32, Hkv=8, D=128, bs=16, kv_dtype="i4", lengths=[40, 9, 300, 16, 130], seed=81)
     counts = w.query_counts(6)

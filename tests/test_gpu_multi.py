@@ -163,45 +163,3 @@ def test_full_size_chunk_sampled():
     err = max_err(out[torch.from_numpy(rows).to(DEV)], want)
     say(f"  sampled seqs {picks}: max abs err {err:.3e}")
     assert err <= TOL[s.kv_dtype]
-
-
-# shapes that take the wide units (enough rows for two groups per wavefront
-# and enough (sequence, kv head) pairs to fill the GPU):
-# (kv dtype, Hq, Hkv, cached tokens, new tokens, sequences, block size)
-WIDE = [
-    ("bf16", 40, 40, 2048, 512, 8, 16),
-    ("bf16", 64, 8, 1500, 300, 8, 32),
-    ("i8", 32, 8, 2048, 256, 8, 16),
-    ("i4", 32, 8, 1024, 128, 16, 64),
-]
-
-
-@pytest.mark.parametrize("case", range(len(WIDE)))
-def test_wide_units_sampled(case):
-    """Long chunks at full size; sampled query rows (the first, second,
-    middle and last new token of a few sequences, every head) against the
-    oracle's decode on the context truncated at the row's own position."""
-    kv, Hq, Hkv, L, n, B, bs = WIDE[case]
-    lens = [L - 37 * i for i in range(B)]
-    w = make_custom(B=B, Hq=Hq, Hkv=Hkv, D=128, bs=bs, kv_dtype=kv, lengths=lens, seed=90 + case)
-    s = w.spec
-    say(f"[multi wide] {kv} Hq={Hq} Hkv={Hkv} L<={L} n={n} B={B} bs={bs}")
-    from workloads.device import append_tokens
-    cache = pa.KVCache.allocate(w.num_blocks, Hkv, bs, 128, kv, DEV)
-    append_tokens(w, cache)
-    counts = np.full(B, n, np.int32)
-    q_start, q = w.multi_queries(counts)
-    out = _multi_gpu(w, cache, q_start, q, n)
-    assert torch.all(torch.isfinite(out))
-    picks = [0, B // 2, B - 1]
-    oc = oracle.build_cache(w, seqs=picks)
-    worst = 0.0
-    for b in picks:
-        Lb = int(w.context_lens[b])
-        for i in (0, 1, n // 2, n - 1):
-            row = int(q_start[b]) + i
-            want = oracle.decode(q[row:row + 1], oc, w.block_tables[b:b + 1], np.array([Lb - n + i + 1], np.int32),
-                                 s.scale)
-            worst = max(worst, max_err(out[row:row + 1], want))
-    say(f"  sampled rows: max abs err {worst:.3e}")
-    assert worst <= TOL[kv]

@@ -1,5 +1,4 @@
 """HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
-import math
 
 import numpy as np
 import pytest
@@ -222,44 +221,6 @@ def test_split_partition_sweep_agrees():
     for P in (64, 128, 512, 4096):
         _, _, out, _ = _split_gpu(w, cache, P)
         assert max_err(out, want) <= TOL["bf16"], P
-
-
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_sampled(cfg):
-    """Full-size workload, cache written by the GPU append, then the step the
-    benchmark times (pa_append_decode, or pa_append_decode_split + pa_reduce
-    for the KV-split workload); sampled sequences checked against the oracle."""
-    from workloads.device import new_token_batch
-
-    w = make_workload(cfg)
-    s = w.spec
-    say(f"[full] cfg{cfg} B={w.B} tokens={w.total_tokens()} pool={w.num_blocks}")
-    cache = poisoned_cache(w)
-    gpu_append_tokens(w, cache, include_last=False)
-    kn, vn, sl = new_token_batch(w)
-    q, tables, lens = meta(w)
-    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
-    if s.partition_size:
-        pmax = pa.max_partitions(tables.shape[1], s.bs, s.partition_size)
-        B, Hq, D = q.shape
-        po = torch.full((B, Hq, pmax, D), SENTINEL, dtype=torch.float32, device=DEV)
-        pl = torch.full((B, Hq, pmax), SENTINEL, dtype=torch.float32, device=DEV)
-        pa.append_decode_split(kn, vn, sl, q, cache, tables, lens, s.scale, s.partition_size, po, pl)
-        pa.reduce(po, pl, lens, s.partition_size, out)
-    else:
-        pa.append_decode(kn, vn, sl, q, cache, tables, lens, s.scale, out)
-    torch.cuda.synchronize()
-    assert torch.all(torch.isfinite(out))
-    rng = np.random.default_rng(cfg)
-    picks = sorted(set(rng.choice(w.B, size=min(3, w.B), replace=False).tolist()) | {int(np.argmax(w.context_lens))})
-    if w.pair_of:
-        b2, a = next(iter(w.pair_of.items()))
-        picks = sorted(set(picks) | {a, b2})
-    oc = oracle.build_cache(w, seqs=sorted(set(picks) | {w.pair_of[b] for b in picks if b in w.pair_of}))
-    want = oracle.decode(w.q[picks], oc, w.block_tables[picks], w.context_lens[picks], s.scale)
-    err = max_err(out[picks], want)
-    say(f"  sampled seqs {picks}: max abs err {err:.3e}")
-    assert err <= TOL[s.kv_dtype]
 
 
 def test_int8_full_cache_fill_bit_exact():

@@ -95,6 +95,7 @@ class WorkloadSpec:
     len_hi: int = 0
     ln_median: float = 512.0
     ln_sigma: float = 0.9
+    v_scale: float = 1.0  # V draws multiplied by this (a power of two keeps them exact in bf16)
 
     @property
     def G(self) -> int:
@@ -188,6 +189,8 @@ class Workload:
             n_peak = int(round(s.peak_frac * L))
             pos = rng.choice(L, size=n_peak, replace=False)
             K[pos] *= np.float32(s.peak_scale)
+        if s.v_scale != 1.0:
+            V *= np.float32(s.v_scale)
         return self._store(K), self._store(V)
 
     def tokens(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -201,7 +204,7 @@ class Workload:
                 rng = self._rng(2, b)
                 s = self.spec
                 kn = rng.standard_normal((s.Hkv, s.D), dtype=np.float32)
-                vn = rng.standard_normal((s.Hkv, s.D), dtype=np.float32)
+                vn = rng.standard_normal((s.Hkv, s.D), dtype=np.float32) * np.float32(s.v_scale)
                 K[L - 1] = self._store(kn)
                 V[L - 1] = self._store(vn)
             return K, V
@@ -346,7 +349,8 @@ def make_workload(cfg: int, seed: Optional[int] = None, small: bool = False, **o
 def make_custom(*, B: int, Hq: int, Hkv: int, D: int, bs: int, kv_dtype: str, q_dtype: Optional[str] = None,
                 lengths: Sequence[int], seed: int = 7, scale: Optional[float] = None, max_len: Optional[int] = None,
                 pool_factor: float = 1.2, pool_blocks: Optional[int] = None, beam_pair_frac: float = 0.0,
-                peak_frac: float = 0.0, partition_size: Optional[int] = None, cfg: int = 99) -> Workload:
+                peak_frac: float = 0.0, partition_size: Optional[int] = None, cfg: int = 99,
+                v_scale: float = 1.0) -> Workload:
     """A workload with explicit lengths and shapes (edge cases, sweeps)."""
     q_dtype = q_dtype or ("f32" if kv_dtype == "f32" else "bf16")
     lengths = tuple(int(x) for x in lengths)
@@ -355,6 +359,6 @@ def make_custom(*, B: int, Hq: int, Hkv: int, D: int, bs: int, kv_dtype: str, q_
         scale=(1.0 / math.sqrt(D)) if scale is None else float(scale),
         max_len=max(max_len or 0, max(lengths, default=0), 1), partition_size=partition_size,
         pool_blocks=pool_blocks, pool_factor=pool_factor, beam_pair_frac=beam_pair_frac,
-        peak_frac=peak_frac, lengths=lengths, len_dist="explicit",
+        peak_frac=peak_frac, lengths=lengths, len_dist="explicit", v_scale=float(v_scale),
     )
     return _build(spec, seed)
