@@ -236,8 +236,16 @@ def time_case(case: Case, steps: int, warmup: int, flush) -> dict:
     step = _timed(torch, case.step, steps, warmup, flush)
     wall = time.perf_counter() - t0
     r = {"step": stats_us(step), "wall_ms_per_step_incl_flush": 1e3 * wall / steps}
-    for name, fn in case.kernels().items():
+    ks = case.kernels()
+    for name, fn in ks.items():
         r[name] = stats_us(_timed(torch, fn, steps, warmup, flush))
+    if "decode" in ks and case.s.kv_dtype == "bf16" and case.s.D == 128 and case.s.G <= 16:
+        # arithmetic A/B: the same pa_decode on the vector ALUs (PA_DECODE_VALU=1)
+        os.environ["PA_DECODE_VALU"] = "1"
+        try:
+            r["decode_valu"] = stats_us(_timed(torch, ks["decode"], steps, warmup, flush))
+        finally:
+            del os.environ["PA_DECODE_VALU"]
     return r
 
 

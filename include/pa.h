@@ -152,6 +152,12 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, pa_dtype src_
  * Preconditions (device data): 0 <= L <= max_blocks_per_seq * block_size;
  * the first ceil(L / block_size) entries of each row are < num_blocks.
  * num_seqs == 0 is a no-op.
+ * Arithmetic unit: the products run on the matrix cores.  With the
+ * environment variable PA_DECODE_VALU set to "1" (read at every call), a
+ * bf16 cache with head_dim 128 and at most 16 query heads per kv head runs
+ * them on the vector ALUs instead (v_dot2 over bf16 pairs, the same fp32
+ * accumulation and results within the same tolerance): a measurement
+ * switch, slower on every measured shape.
  */
 pa_status pa_decode(const void *q, pa_dtype q_dtype, int32_t num_seqs, int32_t num_heads, const pa_kv_cache *cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens, float scale,

@@ -30,6 +30,7 @@ SOURCES = [
     "pa_noalloc.hip",
     "pa_probe.hip",
     "pa_mla.hip",
+    "pa_decode_valu.hip",
     "pa_block_manager.cpp",
 ]
 

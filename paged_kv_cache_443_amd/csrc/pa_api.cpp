@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include <hip/hip_runtime_api.h>
 
@@ -71,6 +72,13 @@ pa::AppendParams make_append_params(const void *key, const void *value, const in
 // can touch (the table row, or one partition), at most kMaxTableWindow.
 constexpr int32_t kMaxTableWindow = 1024;
 
+// PA_DECODE_VALU=1: single-token bf16 decodes run on the vector ALUs
+// instead of the matrix cores (read at every call, so a process can time both).
+bool valu_requested() {
+  const char *v = std::getenv("PA_DECODE_VALU");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
 int32_t table_window(int32_t max_blocks_per_seq, int32_t partition_size, int32_t block_size) {
   int32_t w = max_blocks_per_seq;
   if (partition_size > 0) w = std::min(w, partition_size / block_size);
@@ -87,6 +95,8 @@ pa_status launch(pa::DecodeParams &p, const pa_kv_cache *cache, hipStream_t stre
   hipError_t e;
   if (cache->kv_dtype == PA_F32)
     e = pa::launch_decode_f32(p, cache->head_dim, cache->block_size, stream);
+  else if (valu_requested() && pa::decode_valu_applies(p, cache->kv_dtype, cache->head_dim))
+    e = pa::launch_decode_valu(p, cache->head_dim, cache->block_size, stream);
   else
     e = pa::launch_decode_mfma(p, cache->kv_dtype, cache->head_dim, cache->block_size, stream);
   return from_hip(e);

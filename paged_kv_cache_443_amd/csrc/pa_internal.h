@@ -153,6 +153,10 @@ hipError_t noalloc_scratch(void **ptr);
 // Launchers (one per kernel family); each returns the launch's hipError_t.
 hipError_t launch_decode_mfma(const DecodeParams &p, pa_dtype kv_dtype, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);
+// Single-token decode of a bf16 cache on the vector ALUs (the arithmetic
+// alternative to the matrix cores; pa_decode takes it when PA_DECODE_VALU=1).
+bool decode_valu_applies(const DecodeParams &p, pa_dtype kv_dtype, int head_dim);
+hipError_t launch_decode_valu(const DecodeParams &p, int head_dim, int block_size, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, pa_dtype kv_dtype, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t s);

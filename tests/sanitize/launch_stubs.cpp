@@ -14,6 +14,8 @@ namespace pa {
 
 hipError_t launch_decode_mfma(const DecodeParams &, pa_dtype, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode_f32(const DecodeParams &, int, int, hipStream_t) { return hipErrorNoDevice; }
+bool decode_valu_applies(const DecodeParams &, pa_dtype, int) { return false; }
+hipError_t launch_decode_valu(const DecodeParams &, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_reduce(const ReduceParams &, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_append(const AppendParams &, pa_dtype, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_copy_blocks(const CopyParams &, hipStream_t) { return hipErrorNoDevice; }
