@@ -724,7 +724,9 @@ def main(argv=None) -> int:
     log(f"copy_blocks: {copy_stats}")
     swap_stats = time_swap(case, min(args.steps, 10), min(args.warmup, 2))
     log(f"swap_blocks: {swap_stats}")
-    multi_stats = time_multi(case, args.steps, args.warmup, flush, perfmodel) if not case.split else {}
+    # causal multi-query decode: quantised and bf16 caches (not the KV-split or fp32 workloads)
+    multi = not case.split and case.s.kv_dtype != "f32"
+    multi_stats = time_multi(case, args.steps, args.warmup, flush, perfmodel) if multi else {}
     log(f"decode_multi: {multi_stats}")
 
     s = case.s

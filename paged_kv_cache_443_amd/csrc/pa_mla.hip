@@ -30,13 +30,19 @@
 //       w % 4 (16 tokens) over latent half w / 4; the two halves' partial
 //       scores meet in LDS.  A = 16 latent rows (16-byte LDS reads), B = the
 //       wave's half of Q_lat as bf16 hi + lo parts (held in VGPRs).
+//   softmax  waves 0-3 (one 16-token row group each) scale and mask the
+//       scores, publish their row group's maxima, and every wave reads the
+//       chunk maximum of each head from LDS (the same value in every wave);
+//       waves 0-3 then write P as bf16 hi + lo parts to LDS and keep the
+//       running sums.
 //   PV  O^T[dim][head] += C^T[dim][token] P^T[token][head]   wave w: latent
-//       dims 64w .. 64w + 63 over all 64 tokens.  A = C^T (16-bit LDS reads,
-//       the staged rows read down a column), B = P as bf16 hi + lo.
-// Every wavefront computes the same softmax statistics from the same scores
-// (bit for bit), so the eight dimension slices need no merge: each wave
-// writes its own 64 dims of the partial output.  The latent rows of the
-// next two chunks are in flight in VGPRs while one chunk is computed.
+//       dims 64w .. 64w + 63 over all 64 tokens.  A = C^T (the staged rows
+//       read down a column as 32-bit words, the wanted halves picked with a
+//       byte permute), B = P as bf16 hi + lo from LDS.
+// Every wave rescales with the same maxima, so the eight dimension slices
+// need no merge: each wave writes its own 64 dims of the partial output.
+// The latent rows of the next two chunks are in flight in VGPRs while one
+// chunk is computed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
