@@ -22,27 +22,30 @@
 // Step 2 streams the cache (the HBM-bound part); steps 1 and 3 touch only
 // the queries, the partials and the two projection matrices.
 //
-// Attention work-group (8 wavefronts) per piece (sequence b, heads
+// Attention work-group (4 wavefronts) per piece (sequence b, heads
 // 16g .. 16g + 15, partition p); the pieces are dealt persistently (the grid
-// holds what the GPU runs at once).  Chunks of 64 tokens are staged in LDS
-// once per work-group (64 KiB) and used twice:
-//   QK  S^T[token][head] = C[token][:] . Q_lat[head][:]   wave w: row group
-//       w % 4 (16 tokens) over latent half w / 4; the two halves' partial
-//       scores meet in LDS.  A = 16 latent rows (16-byte LDS reads), B = the
-//       wave's half of Q_lat as bf16 hi + lo parts (held in VGPRs).
-//   softmax  waves 0-3 (one 16-token row group each) scale and mask the
-//       scores, publish their row group's maxima, and every wave reads the
-//       chunk maximum of each head from LDS (the same value in every wave);
-//       waves 0-3 then write P as bf16 hi + lo parts to LDS and keep the
-//       running sums.
+// holds what the GPU runs at once: two work-groups per CU, each with its own
+// 81 KiB of LDS, so one streams while the other waits at a barrier).
+// Chunks of 64 tokens are staged in LDS once per work-group (66.5 KiB) and
+// used twice:
+//   QK  S^T[token][head] = C[token][:] . Q_lat[head][:]   wave w: row groups
+//       2 (w % 2) and 2 (w % 2) + 1 (16 tokens each) over latent half w / 2;
+//       the two halves' partial scores meet in LDS.  A = 16 latent rows
+//       (16-byte LDS reads), B = the wave's half of Q_lat as bf16 hi + lo
+//       parts (held in VGPRs).
+//   softmax  wave w takes row group w: scales and masks the scores,
+//       publishes the row group's maxima, and every wave reads the chunk
+//       maximum of each head from LDS (the same value in every wave); then
+//       it writes P as bf16 hi + lo parts to LDS and keeps the running sums.
 //   PV  O^T[dim][head] += C^T[dim][token] P^T[token][head]   wave w: latent
-//       dims 64w .. 64w + 63 over all 64 tokens.  A = C^T (the staged rows
-//       read down a column as 32-bit words, the wanted halves picked with a
-//       byte permute), B = P as bf16 hi + lo from LDS.
-// Every wave rescales with the same maxima, so the eight dimension slices
-// need no merge: each wave writes its own 64 dims of the partial output.
-// The latent rows of the next two chunks are in flight in VGPRs while one
-// chunk is computed.
+//       dims 128w .. 128w + 127 over all 64 tokens.  A = C^T (the staged
+//       rows read down a column as 32-bit words, the wanted halves picked
+//       with a byte permute), B = P as bf16 hi + lo from LDS.
+// Every wave rescales with the same maxima, so the four dimension slices
+// need no merge: each wave writes its own 128 dims of the partial output.
+// The latent rows of the next chunk are in flight in VGPRs while one chunk
+// is computed (thread t loads rows t / 8 and t / 8 + 32 of it, whole
+// 128-byte lines per lane octet).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -54,7 +57,7 @@ namespace pa {
 namespace {
 
 constexpr int DC = kMlaLatentDim;                 // 512
-constexpr int NW = 8;                             // wavefronts per attention work-group
+constexpr int NW = 4;                             // wavefronts per attention work-group
 constexpr int NT = NW * 64;
 constexpr int CT = kMlaChunk;                     // 64 tokens per chunk
 constexpr int VPR = DC / 8;                       // 16-byte vectors per latent row: 64
@@ -64,7 +67,7 @@ constexpr int SPAD = CT + 4;                      // floats per staged score row
 constexpr size_t kRowsBytes = static_cast<size_t>(CT) * ROW;
 constexpr size_t kScoreBytes = static_cast<size_t>(2) * 16 * SPAD * 4;
 static_assert(VPT * NT == CT * VPR, "a chunk is a whole number of vectors per thread");
-static_assert(NT / 8 == CT && 8 * VPT == VPR, "thread t stages row t / 8, vectors t % 8 + 8 i");
+static_assert(NT / 8 == CT / 2 && VPT == 16, "thread t stages rows t / 8 and t / 8 + 32, vectors t % 8 + 8 i");
 
 // Staged row r keeps its 16-byte vector v at v ^ swz(r): the four 8-row
 // groups of a 32-token k-step land on different banks when PV reads down a
@@ -153,46 +156,53 @@ struct MlaSmem {
 template <int BS>
 __device__ __forceinline__ void mla_issue(u32x4 (&R)[VPT], const MlaParams &p, const int32_t *tbl, int lb0, int cs,
                                           int t1) {
-  const int tok = min(cs + static_cast<int>(threadIdx.x >> 3), t1 - 1);
-  // out-of-range table entries are clamped so that a bad table can never fault
-  const uint32_t pb = min(static_cast<uint32_t>(tbl[tok / BS - lb0]), static_cast<uint32_t>(p.num_blocks - 1));
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(p.cache) + (static_cast<size_t>(pb) * BS + tok % BS) * VPR +
-                     (threadIdx.x & 7);
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) R[i] = __builtin_nontemporal_load(src + 8 * i);
+  for (int hr = 0; hr < 2; ++hr) {
+    const int tok = min(cs + static_cast<int>(threadIdx.x >> 3) + 32 * hr, t1 - 1);
+    // out-of-range table entries are clamped so that a bad table can never fault
+    const uint32_t pb = min(static_cast<uint32_t>(tbl[tok / BS - lb0]), static_cast<uint32_t>(p.num_blocks - 1));
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.cache) + (static_cast<size_t>(pb) * BS + tok % BS) * VPR +
+                       (threadIdx.x & 7);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R[8 * hr + i] = __builtin_nontemporal_load(src + 8 * i);
+  }
 }
 
 template <int BS>
 __device__ __forceinline__ void mla_stage(u32x4 (&R)[VPT], const MlaSmem &sm, int cs, int t1) {
-  const int r = static_cast<int>(threadIdx.x >> 3);
-  if (cs + CT > t1 && cs + r >= t1) {  // rows past the range: zero, never NaN
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) R[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int hr = 0; hr < 2; ++hr) {
+    const int r = static_cast<int>(threadIdx.x >> 3) + 32 * hr;
+    if (cs + CT > t1 && cs + r >= t1) {  // rows past the range: zero, never NaN
+#pragma unroll
+      for (int i = 0; i < 8; ++i) R[8 * hr + i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    unsigned char *row = sm.rows + static_cast<size_t>(r) * ROW;
+    const int sw = swz(r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4 *>(row + ((static_cast<int>(threadIdx.x & 7) + 8 * i) ^ sw) * 16) = R[8 * hr + i];
   }
-  unsigned char *row = sm.rows + static_cast<size_t>(r) * ROW;
-  const int sw = swz(r);
-#pragma unroll
-  for (int i = 0; i < VPT; ++i)
-    *reinterpret_cast<u32x4 *>(row + ((static_cast<int>(threadIdx.x & 7) + 8 * i) ^ sw) * 16) = R[i];
 }
 
 struct MlaState {
-  f32x4 acc[4];  // O^T[64w + 16n + 4j + i][head m]
-  float m_run;   // running maximum (log2 domain), head m (the same in every wavefront)
-  float l_run;   // waves 0-3: this lane's share of the running sum of its row group
+  f32x4 acc[8];  // O^T[128w + 16n + 4j + i][head m]
+  float m_run;   // running maximum (log2 domain), head m (the same in every wave)
+  float l_run;   // this lane's share of the running sum of the wave's row group
 };
 
-// One chunk staged in LDS: QK (every wave: a row group over a latent half),
-// softmax (waves 0-3: one row group each; the chunk maximum through LDS),
-// the probabilities through LDS, PV (every wave: its 64 latent dims).
+// One chunk staged in LDS: QK (every wave: two row groups over a latent
+// half), softmax (wave w: row group w; the chunk maximum through LDS), the
+// probabilities through LDS, PV (every wave: its 128 latent dims).
 __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, const bf16x8 (&qh)[8],
                                             const bf16x8 (&ql)[8], int cs, int t1, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int m = lane & 15, j = lane >> 4;
-  {
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
     // QK partial over latent half hf for row group rg
-    const int rg = w & 3, hf = w >> 2;
+    const int rg = 2 * (w & 1) + rr, hf = w >> 1;
     const int r = 16 * rg + m;
     f32x4 Sh = f32x4{0.f, 0.f, 0.f, 0.f}, Sl = Sh;  // two accumulation chains (hi and lo parts of Q_lat)
     const unsigned char *arow = sm.rows + static_cast<size_t>(r) * ROW;
@@ -208,8 +218,8 @@ __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, con
     *reinterpret_cast<f32x4 *>(sm.sc + (hf * 16 + m) * SPAD + 16 * rg + 4 * j) = Sh + Sl;
   }
   lds_barrier();
-  f32x4 sv;  // waves 0-3: scores (log2 domain) of tokens 16 w + 4 j + i, head m
-  if (w < 4) {
+  f32x4 sv;  // scores (log2 domain) of tokens 16 w + 4 j + i, head m
+  {
     const f32x4 a = *reinterpret_cast<const f32x4 *>(sm.sc + m * SPAD + 16 * w + 4 * j);
     const f32x4 b = *reinterpret_cast<const f32x4 *>(sm.sc + (16 + m) * SPAD + 16 * w + 4 * j);
     float mx = -INFINITY;
@@ -228,8 +238,8 @@ __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, con
   const float alpha = fast_exp2(st.m_run - m_new);  // 0 when m_run is -inf
   st.m_run = m_new;
 #pragma unroll
-  for (int n = 0; n < 4; ++n) st.acc[n] *= alpha;
-  if (w < 4) {
+  for (int n = 0; n < 8; ++n) st.acc[n] *= alpha;
+  {
     float psum = 0.f;
     uint32_t hi[2], lo[2];
 #pragma unroll
@@ -247,21 +257,21 @@ __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, con
     *reinterpret_cast<u32x2 *>(sm.pl + m * PPAD + 16 * w + 4 * j) = u32x2{lo[0], lo[1]};
   }
   lds_barrier();
-  // PV over this wave's 64 latent dims
+  // PV over this wave's 128 latent dims
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     // B = P^T: lane (head m, j) takes tokens 32 ks + 8 j .. + 7
     const bf16x8 phi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sm.ph + m * PPAD + 32 * ks + 8 * j));
     const bf16x8 plo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sm.pl + m * PPAD + 32 * ks + 8 * j));
-    // A = C^T: lane (dim 64 w + 16 n + m, j) needs rows 32 ks + 8 j + e of its
+    // A = C^T: lane (dim 128 w + 16 n + m, j) needs rows 32 ks + 8 j + e of its
     // column.  It reads the 32-bit word holding its dim and its neighbour
     // (no 16-bit loads merging into one register, which serialise) and keeps
     // its half; all rows of the k-step share the swizzle 2 j.
     const unsigned char *col = sm.rows + static_cast<size_t>(32 * ks + 8 * j) * ROW + ((m & 7) >> 1) * 4;
     const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two words
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int v = (8 * w + 2 * n + (m >> 3)) ^ (2 * j);
+    for (int n = 0; n < 8; ++n) {
+      const int v = (16 * w + 2 * n + (m >> 3)) ^ (2 * j);
       uint32_t wd[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) wd[e] = *reinterpret_cast<const uint32_t *>(col + static_cast<size_t>(e) * ROW + v * 16);
@@ -293,7 +303,7 @@ __device__ __forceinline__ void mla_piece(const MlaParams &p, const MlaSmem &sm,
   // the wave's latent half of its 16 heads' absorbed queries, as bf16 hi + lo
   const int h = 16 * g + m;
   const bool hvalid = h < p.num_heads;
-  const int hf = w >> 2;
+  const int hf = w >> 1;
   bf16x8 qh[8], ql[8];
   {
     const float *qrow = p.q_lat + (static_cast<size_t>(b) * p.num_heads + (hvalid ? h : 0)) * DC + 256 * hf + 8 * j;
@@ -319,61 +329,46 @@ __device__ __forceinline__ void mla_piece(const MlaParams &p, const MlaSmem &sm,
   }
   MlaState st;
 #pragma unroll
-  for (int n = 0; n < 4; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = -INFINITY;
   st.l_run = 0.f;
   __syncthreads();  // table window staged
 
-  // Two chunks in flight ahead of the one computed.  The loads are issued on
+  // One chunk in flight ahead of the one computed.  The loads are issued on
   // every path, past the end too (clamped to position t1 - 1: valid rows,
-  // never used), so that the two buffers' loads are always outstanding in the
-  // same order and waiting for one buffer never drains the other.  The
-  // barriers inside the loop wait for LDS only, so the loads stay in flight
-  // across them.
+  // never used), so the compiler never has to wait for loads it cannot
+  // count.  The barriers inside the loop wait for LDS only, so the loads
+  // stay in flight across them.
   const int nch = (t1 - t0 + CT - 1) / CT;
-  u32x4 RA[VPT], RB[VPT];
+  u32x4 RA[VPT];
   mla_issue<BS>(RA, p, sm.tbl, lb0, t0, t1);
-  __builtin_amdgcn_sched_barrier(0);  // every load of A before any of B, as in the loop
-  mla_issue<BS>(RB, p, sm.tbl, lb0, t0 + CT, t1);
   __builtin_amdgcn_sched_barrier(0);
-  for (int k = 0; k < nch; k += 2) {
-    {
-      const int cs = t0 + k * CT;
-      lds_barrier();  // the previous chunk's LDS readers are done
-      mla_stage<BS>(RA, sm, cs, t1);
-      __builtin_amdgcn_sched_barrier(0);
-      mla_issue<BS>(RA, p, sm.tbl, lb0, cs + 2 * CT, t1);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();  // chunk staged
-      mla_compute(st, sm, qh, ql, cs, t1, p.scale_log2);
-    }
-    {
-      const int cs = t0 + (k + 1) * CT;
-      lds_barrier();
-      mla_stage<BS>(RB, sm, cs, t1);
-      __builtin_amdgcn_sched_barrier(0);
-      mla_issue<BS>(RB, p, sm.tbl, lb0, cs + 2 * CT, t1);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      if (k + 1 < nch) mla_compute(st, sm, qh, ql, cs, t1, p.scale_log2);  // uniform
-    }
+  for (int k = 0; k < nch; ++k) {
+    const int cs = t0 + k * CT;
+    lds_barrier();  // the previous chunk's LDS readers are done
+    mla_stage<BS>(RA, sm, cs, t1);
+    __builtin_amdgcn_sched_barrier(0);
+    mla_issue<BS>(RA, p, sm.tbl, lb0, cs + CT, t1);  // past the end: clamped, valid, unused
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();  // chunk staged
+    mla_compute(st, sm, qh, ql, cs, t1, p.scale_log2);
   }
 
-  // the running sum: waves 0-3 hold their row groups' shares (lanes j of a head split them)
-  if (w < 4) {
+  // the running sum: each wave holds its row group's share (lanes j of a head split them)
+  {
     float l = st.l_run + __shfl_xor(st.l_run, 16);
     l = l + __shfl_xor(l, 32);
     if (j == 0) sm.gsum[w * 16 + m] = l;
   }
   __syncthreads();
   const float l = (sm.gsum[m] + sm.gsum[16 + m]) + (sm.gsum[32 + m] + sm.gsum[48 + m]);
-  // normalised partial output of this wave's 64 dims, and the log-sum-exp
+  // normalised partial output of this wave's 128 dims, and the log-sum-exp
   if (hvalid) {
     const size_t prow = (static_cast<size_t>(b) * p.num_heads + h) * p.max_num_partitions + part;
     const float inv = 1.f / l;  // l >= 1: the maximum's own term
-    float *o = p.part_out + prow * DC + 64 * w + 4 * j;
+    float *o = p.part_out + prow * DC + 128 * w + 4 * j;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4 *>(o + 16 * n) = st.acc[n] * inv;
+    for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4 *>(o + 16 * n) = st.acc[n] * inv;
     if (w == 0 && j == 0) p.part_lse[prow] = (st.m_run + __log2f(l)) * kLn2;
   }
 }
@@ -382,7 +377,7 @@ __device__ __forceinline__ void mla_piece(const MlaParams &p, const MlaSmem &sm,
 // non-empty (sequence, head group, partition) pieces, counted per sequence
 // and prefix-summed in LDS.
 template <int BS>
-__global__ __launch_bounds__(NT) void mla_attn_kernel(MlaParams p, int tbl_window) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void mla_attn_kernel(MlaParams p, int tbl_window) {
   extern __shared__ __align__(16) unsigned char smem[];
   MlaSmem sm;
   sm.rows = smem;
