@@ -1089,6 +1089,273 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
   return (blk * 8 + in % nb) * HG + in / nb;
 }
 
+// ---- single-token units with two row groups per wavefront (MQA-like groups) --
+// Every wavefront holds both row groups of the unit and takes every NW-th
+// chunk of the tokens, so each K/V fragment it loads (and, int8 / int4,
+// converts) feeds both groups' products.  With the groups on separate
+// wavefronts (R = 2 units) every fragment was loaded and converted twice; the
+// int8 MQA-like decode was bound by those conversions.  The states are merged
+// through LDS one row group at a time.  Eight wavefronts per unit: 233 (bf16),
+// 254 (int8) and 225 (int4) VGPRs, no spills, one work-group per CU.
+
+// QK of both row groups off each converted K fragment (converted once).
+template <int KV, int D>
+__device__ __forceinline__ void qk_rw(Scores<KV, D> (&S)[2], const KBuf<KV, D> &kb, const QOp<KV, D> (&qop)[2]) {
+  using T = Tile<KV, D>;
+#pragma unroll
+  for (int q = 0; q < T::NQ; ++q) {
+    S[0].s[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    S[1].s[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T::NS; ++s) {
+      bf16x8 a;
+      if constexpr (KV == kInt8) {
+        const u32x4 w = kb.k[q][s >> 1];
+        a = (s & 1) ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else if constexpr (KV == kInt4) {
+        const u32x2 w = kb.k[q][s >> 1];
+        a = i4x8_to_bf16x8_biased((s & 1) ? w[1] : w[0]);
+      } else {
+        a = __builtin_bit_cast(bf16x8, kb.k[q][s]);
+      }
+      S[0].s[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0].q[s], S[0].s[q], 0, 0, 0);
+      S[1].s[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1].q[s], S[1].s[q], 0, 0, 0);
+    }
+  }
+}
+
+// PV of both row groups off each converted V fragment (P as pv_update packs it).
+template <int KV, int D, bool TAIL>
+__device__ __forceinline__ void pv_rw(State<KV, D> (&st)[2], VBuf<KV, D> &vb, const Probs<KV, D> (&P)[2], int tok0,
+                                      int t1) {
+  using T = Tile<KV, D>;
+  constexpr bool LO = KV != kInt4;
+  if constexpr (TAIL && !kQuant<KV>) {
+    uint32_t keep[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      keep[k] = ((tok0 + 2 * k < t1) ? 0x0000ffffu : 0u) | ((tok0 + 2 * k + 1 < t1) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int n = 0; n < T::ND; ++n)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vb.v[n][k] &= keep[k];
+  }
+#pragma unroll
+  for (int r = 0; r < T::NR; ++r) {
+    bf16x8 phi[2], plo[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = P[g].p[8 * r + (KV == kInt4 ? kEvenFirst[e] : e)];
+        const __bf16 h = static_cast<__bf16>(f);
+        phi[g][e] = h;
+        if constexpr (LO) {
+          const __bf16 lo = static_cast<__bf16>(f - static_cast<float>(h));
+          plo[g][e] = lo;
+        } else if constexpr (KV == kInt4) {
+          st[g].vsum += static_cast<float>(h);
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < T::ND; ++n) {
+      bf16x8 a;
+      if constexpr (KV == kInt8) {
+        const u32x4 w = vb.v[n];
+        a = r ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+      } else if constexpr (KV == kInt4) {
+        const u32x2 w = vb.v[n];
+        a = i4x8_to_bf16x8_biased(r ? w[1] : w[0]);
+      } else {
+        a = __builtin_bit_cast(bf16x8, vb.v[n]);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        st[g].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[g], st[g].acc[n], 0, 0, 0);
+        if constexpr (LO) st[g].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[g], st[g].acc[n], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int KV, int D, int BS, bool TAIL, bool REFILL>
+__device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &kb, VBuf<KV, D> &vb,
+                                           const Ctx<KV, D, BS> &x, const QOp<KV, D> (&qop)[2], int cs, int cn,
+                                           Ids idn, float scale_log2) {
+  using T = Tile<KV, D>;
+  Scores<KV, D> S[2];
+  qk_rw<KV, D>(S, kb, qop);
+  if constexpr (REFILL) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k<true>(kb, x, cn, idn);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  Probs<KV, D> P[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    softmax<KV, D, TAIL>(st[r], S[r], vb, P[r], cs + T::TPL * x.j, x.t1, scale_log2, qop[r].bias);
+  pv_rw<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
+  if constexpr (REFILL) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_v<true>(vb, x, cn, idn);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int KV, int D, int BS, int NW, bool CAUSAL>
+__device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &sm, int b, int hx) {
+  using T = Tile<KV, D>;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int kvh = hx / p.head_groups;   // p.head_groups: units per kv head here
+  const int rg0 = (hx % p.head_groups) * 2;
+  const int nrows = p.group;
+  // a multi-query launch bounded to one new token per sequence: the query row
+  // of sequence b is q_start[b] (a sequence with none, or out-of-bounds
+  // offsets, is skipped; uniform over the work-group, before any barrier)
+  int qb = b;
+  if constexpr (CAUSAL) {
+    qb = p.q_start[b];
+    const int nq = p.q_start[b + 1] - qb;
+    if (nq < 1 || qb < 0 || qb + nq > p.num_queries || nq > p.max_q_len) return;
+  }
+  const int TW = p.tbl_window;
+  const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const int Lraw = p.context_lens[b];
+  {
+    const int n_first = min(TW, p.max_blocks_per_seq);
+    for (int i = threadIdx.x; i < n_first; i += NW * 64) sm.tbl[i] = table[i];
+  }
+  const int L = min(max(Lraw, 0), p.max_blocks_per_seq * BS);
+  Ctx<KV, D, BS> x;
+  x.m = lane & 15;
+  x.j = lane >> 4;
+  x.kvh = kvh;
+  x.hkv = p.num_kv_heads;
+  x.num_blocks_m1 = p.num_blocks - 1;
+  x.kpool = static_cast<const typename KvVec<KV>::T *>(p.k_cache);
+  x.vpool = static_cast<const typename KvVec<KV>::T *>(p.v_cache);
+  x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
+  x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
+  x.tbl = sm.tbl;
+  x.t1 = L;
+  x.nbv = (L + BS - 1) / BS;
+  x.newpos = -1;
+  x.newblk = -1;
+  x.newk = 0u;
+  x.newv = 0u;
+  x.news = 0u;
+  x.scr = nullptr;
+  QOp<KV, D> qop[2];
+  int gc[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int r0 = (rg0 + r) * 16;
+    gc[r] = min(16, nrows - r0);  // <= 0: a row group past the last head
+    const bool qvalid = x.m < gc[r];
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(qb) * p.num_heads + kvh * p.group + r0 + x.m) * D;
+#pragma unroll
+    for (int s = 0; s < T::NS; ++s) {
+      const int d0 = kQuant<KV> ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4 *>(qrow + d0);
+      qop[r].q[s] = __builtin_bit_cast(bf16x8, v);
+    }
+    prepare_qop(qop[r]);
+  }
+  State<KV, D> st[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int n = 0; n < T::ND; ++n) st[r].acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st[r].m_run = -INFINITY;
+    st[r].l_run = 0.f;
+    st[r].vsum = 0.f;
+  }
+  __syncthreads();
+  constexpr int STEP = NW * T::CT;
+  for (int ws = 0; ws < L; ws += TW * BS) {
+    const int we = min(ws + TW * BS, L);
+    x.lb0 = ws / BS;
+    if (ws != 0) {
+      const int nbw = (we + BS - 1) / BS - x.lb0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < nbw; i += NW * 64) sm.tbl[i] = table[x.lb0 + i];
+      __syncthreads();
+    }
+    const int nch = (we - ws + T::CT - 1) / T::CT;
+    const int n = w < nch ? (nch - w + NW - 1) / NW : 0;
+    if (n > 0) {
+      KBuf<KV, D> kb;
+      VBuf<KV, D> vb;
+      int cs = ws + w * T::CT;
+      const Ids ids = read_ids(x, cs);
+      issue_k<true>(kb, x, cs, ids);
+      issue_v<true>(vb, x, cs, ids);
+      for (int k = 0; k + 1 < n; ++k) {
+        const int cn = cs + STEP;
+        consume_rw<KV, D, BS, false, true>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), p.scale_log2);
+        cs = cn;
+      }
+      consume_rw<KV, D, BS, true, false>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, p.scale_log2);
+    }
+  }
+  // merge the wavefronts' states, one row group at a time (rows = 16)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    finish_state(st[r]);
+    float l = st[r].l_run + __shfl_xor(st[r].l_run, 16);
+    l = l + __shfl_xor(l, 32);
+    if (r == 1) __syncthreads();  // the first group's readers are done with the slots
+    {
+      float *arow = sm.acc + (static_cast<size_t>(w) * 16 + x.m) * (D + 4);
+#pragma unroll
+      for (int n = 0; n < T::ND; ++n) *reinterpret_cast<f32x4 *>(arow + 16 * n + 4 * x.j) = st[r].acc[n];
+      if (x.j == 0) {
+        sm.m[w * 16 + x.m] = st[r].m_run;
+        sm.l[w * 16 + x.m] = l;
+      }
+    }
+    __syncthreads();
+    const int rs0 = (rg0 + r) * 16;
+    for (int e = threadIdx.x; e < max(gc[r], 0) * D; e += NW * 64) {
+      const int gi = e / D;
+      const int d = e % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NW; ++t) M = fmaxf(M, sm.m[t * 16 + gi]);
+      float o = 0.f;
+      if (M != -INFINITY) {
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+          const float f = fast_exp2(sm.m[t * 16 + gi] - M);
+          lsum += f * sm.l[t * 16 + gi];
+          osum += f * sm.acc[(static_cast<size_t>(t) * 16 + gi) * (D + 4) + d];
+        }
+        o = osum / lsum;
+      }
+      const size_t row = static_cast<size_t>(qb) * p.num_heads + kvh * p.group + rs0 + gi;
+      if (p.out_bf16)
+        static_cast<uint16_t *>(p.out)[row * D + d] = float_to_bf16_bits(o);
+      else
+        static_cast<float *>(p.out)[row * D + d] = o;
+    }
+  }
+}
+
+template <int KV, int D, int BS, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void decode_rw_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Smem sm = carve<D, NW>(smem, p.tbl_window, 16);
+  const int HX = p.num_kv_heads * p.head_groups;
+  int rest = xcd_grouped_unit(static_cast<int>(blockIdx.x), p.num_seqs * p.num_kv_heads, p.head_groups);
+  run_unit_rw<KV, D, BS, NW, CAUSAL>(p, sm, rest / HX, rest % HX);
+}
+
+
 // One work-group per unit: (sequence, kv head x query-head group[, partition]).
 // LPT: a single pass over at most kMaxLptSeqs sequences takes the sequences
 // longest first.  The hardware hands out work-groups in index order, so the
@@ -1302,13 +1569,13 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
 // group's tokens between fewer wavefronts, each holding one chunk in flight.
 // Units with several query tokens are compute-heavy: all groups in one unit
 // (R up to the wavefront count; 512-token chunks ran 2.5x faster than one
-// group per unit).  Single-token units stream: two groups per unit (on one kv
-// head with 32 to 128 query heads, bf16 and int8, two per unit beat four or
-// eight by 1.3-2.4x), or one per unit with the units of a kv head sharing its
-// lines through their XCD's L2 when two per unit would leave work-group
-// slots empty (launch_rows).  The choice depends on the launch shape only,
-// so a multi-query launch with one token per sequence is the single-token
-// launch.
+// group per unit).  Single-token units stream: two groups per unit, both held
+// by every wavefront of the unit (decode_rw_kernel: each K/V fragment, loaded
+// and converted once, feeds both groups' products), or one group per unit
+// with the units of a kv head sharing its lines through their XCD's L2 when
+// two per unit would leave CUs without a work-group (launch_rows).  The
+// choice depends on the launch shape only, so a multi-query launch with one
+// token per sequence is the single-token launch.
 // Wide multi-query units: RW row groups per wavefront, NW * RW per unit.
 constexpr int kWideRowGroups = 2;
 
@@ -1350,6 +1617,31 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
     const bool wide = use_wide<KV, D, BS, NW>(p, e);
     if (e != hipSuccess) return e;
     if (wide) return launch_wide<KV, D, BS, NW>(p, s);
+  }
+  // single token, several row groups per kv head: two per unit, held by
+  // every wavefront, when that gives every CU a work-group (measured on one
+  // kv head with 64 query heads, 128 x 4096 tokens: bf16 76.7 -> 63.1 us,
+  // int8 63.6 -> 48.4 us against two groups on separate wavefronts)
+  int cus_rw = 0;
+  if (p.max_q_len <= 1 && rg >= 2) {
+    int dev = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&cus_rw, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e0 != hipSuccess) return e0;
+  }
+  if (p.max_q_len <= 1 && rg >= 2 &&
+      static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * ((rg + 1) / 2) >= cus_rw) {
+    constexpr int NWR = 8;
+    DecodeParams q = p;
+    q.head_groups = (rg + 1) / 2;  // units per kv head
+    const int64_t nwg = static_cast<int64_t>(q.num_kv_heads) * q.head_groups * q.num_seqs;
+    const size_t lds = lds_bytes<D, NWR>(q.tbl_window, 16, 0);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
+                       s, q);
+    return hipGetLastError();
   }
   const int most = p.max_q_len > 1 ? NW : 2;
   // single token (also a multi-query launch bounded to one token, which is
