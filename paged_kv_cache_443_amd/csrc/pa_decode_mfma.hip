@@ -1089,14 +1089,20 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
   return (blk * 8 + in % nb) * HG + in / nb;
 }
 
-// ---- single-token units with two row groups per wavefront (MQA-like groups) --
+// ---- units with two row groups per wavefront (MQA-like groups, short causal
+// row sets such as a few draft tokens) ------------------------------------------
 // Every wavefront holds both row groups of the unit and takes every NW-th
 // chunk of the tokens, so each K/V fragment it loads (and, int8 / int4,
 // converts) feeds both groups' products.  With the groups on separate
 // wavefronts (R = 2 units) every fragment was loaded and converted twice; the
 // int8 MQA-like decode was bound by those conversions.  The states are merged
-// through LDS one row group at a time.  Eight wavefronts per unit: 233 (bf16),
-// 254 (int8) and 225 (int4) VGPRs, no spills, one work-group per CU.
+// through LDS one row group at a time.  Causal rows (query token r / G of the
+// sequence's nq new tokens, head r % G) mask per lane; chunks that end before
+// the unit's first row's position need no mask.  Eight wavefronts per unit,
+// one work-group per CU: head_dim 128 with block size 16 takes 233 / 238
+// (bf16, single token / causal rows) and 225 / 243 (int4) VGPRs, no spills;
+// int8 takes 254 (at block size 32: 256 and a 16-byte spill per lane) and
+// serves single tokens only (with causal rows it spilled more).
 
 // QK of both row groups off each converted K fragment (converted once).
 template <int KV, int D>
@@ -1179,10 +1185,10 @@ __device__ __forceinline__ void pv_rw(State<KV, D> (&st)[2], VBuf<KV, D> &vb, co
   }
 }
 
-template <int KV, int D, int BS, bool TAIL, bool REFILL>
+template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL>
 __device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &kb, VBuf<KV, D> &vb,
-                                           const Ctx<KV, D, BS> &x, const QOp<KV, D> (&qop)[2], int cs, int cn,
-                                           Ids idn, float scale_log2) {
+                                           const Ctx<KV, D, BS> &x, const QOp<KV, D> (&qop)[2], const int (&t1r)[2],
+                                           int cs, int cn, Ids idn, float scale_log2) {
   using T = Tile<KV, D>;
   Scores<KV, D> S[2];
   qk_rw<KV, D>(S, kb, qop);
@@ -1194,7 +1200,8 @@ __device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &k
   Probs<KV, D> P[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
-    softmax<KV, D, TAIL>(st[r], S[r], vb, P[r], cs + T::TPL * x.j, x.t1, scale_log2, qop[r].bias);
+    softmax<KV, D, TAIL, CAUSAL>(st[r], S[r], vb, P[r], cs + T::TPL * x.j, CAUSAL ? t1r[r] : x.t1, scale_log2,
+                                 qop[r].bias);
   pv_rw<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1210,16 +1217,19 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   const int w = threadIdx.x >> 6;
   const int kvh = hx / p.head_groups;   // p.head_groups: units per kv head here
   const int rg0 = (hx % p.head_groups) * 2;
-  const int nrows = p.group;
-  // a multi-query launch bounded to one new token per sequence: the query row
-  // of sequence b is q_start[b] (a sequence with none, or out-of-bounds
+  // causal multi-query: the rows of sequence b are its nq new tokens x G
+  // heads, query rows q_start[b] .. (a unit with no row, or out-of-bounds
   // offsets, is skipped; uniform over the work-group, before any barrier)
-  int qb = b;
+  int qb = b, nq = 1;
   if constexpr (CAUSAL) {
     qb = p.q_start[b];
-    const int nq = p.q_start[b + 1] - qb;
-    if (nq < 1 || qb < 0 || qb + nq > p.num_queries || nq > p.max_q_len) return;
+    nq = p.q_start[b + 1] - qb;
   }
+  const int nrows = nq * p.group;
+  if (CAUSAL && (rg0 * 16 >= nrows || qb < 0 || qb + nq > p.num_queries || nq > p.max_q_len)) return;
+  // rows of several query tokens mask per lane (int8 launches here only with
+  // one token per sequence: its masking code would spill)
+  constexpr bool ROWS = CAUSAL && KV != kInt8;
   const int TW = p.tbl_window;
   const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const int Lraw = p.context_lens[b];
@@ -1239,8 +1249,10 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   x.kscale = reinterpret_cast<const u32x4 *>(p.k_scale);
   x.vscale = reinterpret_cast<const u32x4 *>(p.v_scale);
   x.tbl = sm.tbl;
-  x.t1 = L;
-  x.nbv = (L + BS - 1) / BS;
+  // the unit's positions end at its last row's (all of them for one token)
+  x.t1 = CAUSAL ? min(L, L - nq + (min(nrows, (rg0 + 2) * 16) - 1) / p.group + 1) : L;
+  x.t1_min = L - nq + (rg0 * 16) / p.group + 1;  // the unit's first row sees positions < t1_min
+  x.nbv = (x.t1 + BS - 1) / BS;
   x.newpos = -1;
   x.newblk = -1;
   x.newk = 0u;
@@ -1249,13 +1261,18 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   x.scr = nullptr;
   QOp<KV, D> qop[2];
   int gc[2];
+  int t1r[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int r0 = (rg0 + r) * 16;
-    gc[r] = min(16, nrows - r0);  // <= 0: a row group past the last head
+    gc[r] = min(16, nrows - r0);  // <= 0: a row group past the last row
     const bool qvalid = x.m < gc[r];
+    const int row = r0 + x.m;
+    const int qi = CAUSAL ? row / p.group : 0;
+    const int hq = kvh * p.group + (CAUSAL ? row % p.group : row);
+    t1r[r] = min(L - nq + qi + 1, x.t1);
     const uint16_t *qrow =
-        static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(qb) * p.num_heads + kvh * p.group + r0 + x.m) * D;
+        static_cast<const uint16_t *>(p.q) + (static_cast<size_t>(qb + qi) * p.num_heads + hq) * D;
 #pragma unroll
     for (int s = 0; s < T::NS; ++s) {
       const int d0 = kQuant<KV> ? (64 * (s >> 1) + 16 * x.j + 8 * (s & 1)) : (32 * s + 8 * x.j);
@@ -1276,8 +1293,8 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   }
   __syncthreads();
   constexpr int STEP = NW * T::CT;
-  for (int ws = 0; ws < L; ws += TW * BS) {
-    const int we = min(ws + TW * BS, L);
+  for (int ws = 0; ws < x.t1; ws += TW * BS) {
+    const int we = min(ws + TW * BS, x.t1);
     x.lb0 = ws / BS;
     if (ws != 0) {
       const int nbw = (we + BS - 1) / BS - x.lb0;
@@ -1296,10 +1313,14 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
       issue_v<true>(vb, x, cs, ids);
       for (int k = 0; k + 1 < n; ++k) {
         const int cn = cs + STEP;
-        consume_rw<KV, D, BS, false, true>(st, kb, vb, x, qop, cs, cn, read_ids(x, cn), p.scale_log2);
+        // the unit's earlier rows cannot see all of a chunk past t1_min
+        if (ROWS && cs + T::CT > x.t1_min)
+          consume_rw<KV, D, BS, true, true, ROWS>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
+        else
+          consume_rw<KV, D, BS, false, true, ROWS>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
         cs = cn;
       }
-      consume_rw<KV, D, BS, true, false>(st, kb, vb, x, qop, cs, 0, Ids{0, 0}, p.scale_log2);
+      consume_rw<KV, D, BS, true, false, ROWS>(st, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, p.scale_log2);
     }
   }
   // merge the wavefronts' states, one row group at a time (rows = 16)
@@ -1337,7 +1358,9 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
         }
         o = osum / lsum;
       }
-      const size_t row = static_cast<size_t>(qb) * p.num_heads + kvh * p.group + rs0 + gi;
+      const int rr = rs0 + gi;
+      const int qi = CAUSAL ? rr / p.group : 0;
+      const size_t row = static_cast<size_t>(qb + qi) * p.num_heads + kvh * p.group + (CAUSAL ? rr % p.group : rr);
       if (p.out_bf16)
         static_cast<uint16_t *>(p.out)[row * D + d] = float_to_bf16_bits(o);
       else
@@ -1569,7 +1592,9 @@ hipError_t launch_single(const DecodeParams &p_in, hipStream_t s) {
 // group's tokens between fewer wavefronts, each holding one chunk in flight.
 // Units with several query tokens are compute-heavy: all groups in one unit
 // (R up to the wavefront count; 512-token chunks ran 2.5x faster than one
-// group per unit).  Single-token units stream: two groups per unit, both held
+// group per unit), except a few groups per kv head (below two per
+// wavefront; bf16 and int4), which go two per unit as single-token units do
+// when that fills the GPU.  Single-token units stream: two groups per unit, both held
 // by every wavefront of the unit (decode_rw_kernel: each K/V fragment, loaded
 // and converted once, feeds both groups' products), or one group per unit
 // with the units of a kv head sharing its lines through their XCD's L2 when
@@ -1618,19 +1643,21 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (wide) return launch_wide<KV, D, BS, NW>(p, s);
   }
-  // single token, several row groups per kv head: two per unit, held by
-  // every wavefront, when that gives every CU a work-group (measured on one
-  // kv head with 64 query heads, 128 x 4096 tokens: bf16 76.7 -> 63.1 us,
-  // int8 63.6 -> 48.4 us against two groups on separate wavefronts)
+  // a few row groups per kv head (a single token, or causal rows below the
+  // wide threshold): two per unit, held by every wavefront, when that gives
+  // every CU a work-group (measured on one kv head with 64 query heads,
+  // 128 x 4096 tokens: bf16 76.7 -> 63.1 us, int8 63.6 -> 48.4 us against two
+  // groups on separate wavefronts; 8 draft tokens x 8 heads per kv head,
+  // 32 x 2048 tokens: 75.4 -> 70.2 us against one group per wavefront)
   int cus_rw = 0;
-  if (p.max_q_len <= 1 && rg >= 2) {
+  const bool rw_shape = rg >= 2 && (p.max_q_len <= 1 || (CAUSAL && KV != kInt8 && rg < 2 * NW));
+  if (rw_shape) {
     int dev = 0;
     hipError_t e0 = hipGetDevice(&dev);
     if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&cus_rw, hipDeviceAttributeMultiprocessorCount, dev);
     if (e0 != hipSuccess) return e0;
   }
-  if (p.max_q_len <= 1 && rg >= 2 &&
-      static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * ((rg + 1) / 2) >= cus_rw) {
+  if (rw_shape && static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * ((rg + 1) / 2) >= cus_rw) {
     constexpr int NWR = 8;
     DecodeParams q = p;
     q.head_groups = (rg + 1) / 2;  // units per kv head

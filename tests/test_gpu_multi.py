@@ -74,6 +74,44 @@ def test_multi_matches_oracle(case):
     assert max_err(out2, want) <= TOL[kv]
 
 
+# Launches with enough (sequence, kv head) pairs to fill the GPU (>= 256
+# units): a few row groups per kv head are served two per work-group, held by
+# every wavefront.  Row groups straddle query tokens (G = 3, 5), sequences
+# shorter than their new tokens, empty ones and one new token mix with full
+# ones.
+BIG = [
+    ("bf16", 64, 8, 128, 16, 8, 32),
+    ("bf16", 12, 4, 64, 32, 6, 64),
+    ("bf16", 40, 8, 128, 64, 5, 40),
+    ("i8", 64, 8, 128, 16, 8, 32),
+    ("i8", 24, 4, 64, 32, 6, 64),
+    ("i4", 64, 8, 128, 16, 8, 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BIG)))
+def test_many_units_match_oracle(case):
+    kv, Hq, Hkv, D, bs, mq, B = BIG[case]
+    rng = np.random.default_rng(900 + case)
+    lens = rng.integers(1, 400, size=B)
+    lens[:4] = [0, 1, mq - 1, mq]
+    w = make_custom(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv, lengths=lens.tolist(), seed=60 + case)
+    counts = w.query_counts(mq)
+    counts[5::3] = np.minimum(mq, w.context_lens[5::3])  # a third at the bound
+    q_start, q = w.multi_queries(counts)
+    say(f"[multi many] case {case}: {kv} Hq={Hq} Hkv={Hkv} D={D} bs={bs} max_q={mq} B={B}")
+    oc = oracle.build_cache(w)
+    want = oracle.decode_multi(q, q_start, oc, w.block_tables, w.context_lens, w.spec.scale)
+    cache = upload_oracle_cache(oc)
+    out = _multi_gpu(w, cache, q_start, q, mq)
+    assert torch.all(torch.isfinite(out))
+    err = max_err(out, want)
+    say(f"  max abs err {err:.3e} (tol {TOL[kv]})")
+    assert err <= TOL[kv]
+    ob = _multi_gpu(w, cache, q_start, q, mq, torch.bfloat16)
+    assert torch.equal(ob.view(torch.int16).cpu(), bf16_rne_of(out)), "bf16 out must be RNE of the fp32 out"
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 5, "mqa"])
 def test_one_new_token_is_decode_bitwise(cfg):
     """With one new token per sequence (max_q_len 1) the multi-query path is
