@@ -1185,7 +1185,7 @@ __device__ __forceinline__ void pv_rw(State<KV, D> (&st)[2], VBuf<KV, D> &vb, co
   }
 }
 
-template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL>
+template <int KV, int D, int BS, bool TAIL, bool REFILL, bool CAUSAL, bool NT>
 __device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &kb, VBuf<KV, D> &vb,
                                            const Ctx<KV, D, BS> &x, const QOp<KV, D> (&qop)[2], const int (&t1r)[2],
                                            int cs, int cn, Ids idn, float scale_log2) {
@@ -1194,7 +1194,7 @@ __device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &k
   qk_rw<KV, D>(S, kb, qop);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_k<true>(kb, x, cn, idn);
+    issue_k<NT>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
   Probs<KV, D> P[2];
@@ -1205,12 +1205,12 @@ __device__ __forceinline__ void consume_rw(State<KV, D> (&st)[2], KBuf<KV, D> &k
   pv_rw<KV, D, TAIL>(st, vb, P, cs + T::TPL * x.j, x.t1);
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_v<true>(vb, x, cn, idn);
+    issue_v<NT>(vb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int KV, int D, int BS, int NW, bool CAUSAL>
+template <int KV, int D, int BS, int NW, bool CAUSAL, bool NT>
 __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &sm, int b, int hx) {
   using T = Tile<KV, D>;
   const int lane = threadIdx.x & 63;
@@ -1309,18 +1309,18 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
       VBuf<KV, D> vb;
       int cs = ws + w * T::CT;
       const Ids ids = read_ids(x, cs);
-      issue_k<true>(kb, x, cs, ids);
-      issue_v<true>(vb, x, cs, ids);
+      issue_k<NT>(kb, x, cs, ids);
+      issue_v<NT>(vb, x, cs, ids);
       for (int k = 0; k + 1 < n; ++k) {
         const int cn = cs + STEP;
         // the unit's earlier rows cannot see all of a chunk past t1_min
         if (ROWS && cs + T::CT > x.t1_min)
-          consume_rw<KV, D, BS, true, true, ROWS>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
+          consume_rw<KV, D, BS, true, true, ROWS, NT>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
         else
-          consume_rw<KV, D, BS, false, true, ROWS>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
+          consume_rw<KV, D, BS, false, true, ROWS, NT>(st, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), p.scale_log2);
         cs = cn;
       }
-      consume_rw<KV, D, BS, true, false, ROWS>(st, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, p.scale_log2);
+      consume_rw<KV, D, BS, true, false, ROWS, NT>(st, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, p.scale_log2);
     }
   }
   // merge the wavefronts' states, one row group at a time (rows = 16)
@@ -1369,13 +1369,13 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   }
 }
 
-template <int KV, int D, int BS, int NW, bool CAUSAL>
+template <int KV, int D, int BS, int NW, bool CAUSAL, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_rw_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, 16);
   const int HX = p.num_kv_heads * p.head_groups;
   int rest = xcd_grouped_unit(static_cast<int>(blockIdx.x), p.num_seqs * p.num_kv_heads, p.head_groups);
-  run_unit_rw<KV, D, BS, NW, CAUSAL>(p, sm, rest / HX, rest % HX);
+  run_unit_rw<KV, D, BS, NW, CAUSAL, NT>(p, sm, rest / HX, rest % HX);
 }
 
 
@@ -1661,12 +1661,24 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
     constexpr int NWR = 8;
     DecodeParams q = p;
     q.head_groups = (rg + 1) / 2;  // units per kv head
+    // several units per (sequence, kv head) read the same lines, side by side
+    // on one XCD: ordinary loads, so that all but the first read hit its L2
+    // (64 query heads on one kv head, 128 x 4096 tokens: HBM traffic 1.30x
+    // -> 1.02x the cache bytes, 63.0 -> 57.0 us); one unit: non-temporal
     const int64_t nwg = static_cast<int64_t>(q.num_kv_heads) * q.head_groups * q.num_seqs;
     const size_t lds = lds_bytes<D, NWR>(q.tbl_window, 16, 0);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL>),
+    if (q.head_groups > 1) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
+                         s, q);
+      return hipGetLastError();
+    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
+    hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
                        s, q);
     return hipGetLastError();
   }
