@@ -98,3 +98,37 @@ def test_wide_units_every_sequence(case):
     err = max_err(out[idx], want)
     say(f"  {len(rows)} rows over all {B} sequences: max abs err {err:.3e}")
     assert err <= TOL[kv]
+
+
+def test_wide_units_negative_scale():
+    """A negative softmax scale on the bf16 wide units (they fold the scale
+    into the exponent and take the query's sign instead): sampled rows
+    against the oracle, and the output equals the launch with the query
+    negated and the scale's magnitude, bit for bit."""
+    B, Hq, Hkv, L, n, bs = 8, 64, 8, 1200, 300, 16
+    custom = dict(B=B, Hq=Hq, Hkv=Hkv, D=128, bs=bs, kv_dtype="bf16", lengths=[L - 41 * i for i in range(B)],
+                  seed=97, scale=-0.7 / np.sqrt(128))
+    w = make_custom(**custom)
+    s = w.spec
+    say(f"[multi wide, scale {s.scale:.4f}] Hq={Hq} Hkv={Hkv} L<={L} n={n} B={B}")
+    cache = pa.KVCache.allocate(w.num_blocks, Hkv, bs, 128, "bf16", DEV)
+    append_tokens(w, cache)
+    q_start, q = w.multi_queries(np.full(B, n, np.int32))
+    _, tables, lens = meta(w)
+    qs = torch.from_numpy(q_start).to(DEV)
+
+    def run(qv, scale):
+        out = torch.full((int(q_start[-1]), Hq, 128), SENTINEL, dtype=torch.float32, device=DEV)
+        pa.decode_multi(to_dev_values(qv, s.q_dtype), qs, n, cache, tables, lens, scale, out)
+        torch.cuda.synchronize()
+        return out
+
+    out = run(q, s.scale)
+    assert torch.all(torch.isfinite(out))
+    assert torch.equal(out, run(-q, -s.scale))
+    rows = sorted({(b, i) for b in range(B) for i in (0, 7 * b + 3, n - 1)})
+    want = rows_decode(custom, n, rows, w.context_lens)
+    idx = torch.tensor([int(q_start[b]) + i for b, i in rows], device=DEV)
+    err = max_err(out[idx], want)
+    say(f"  {len(rows)} rows: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
