@@ -226,14 +226,16 @@ pa_status pa_append_decode_split(const void *key, const void *value, pa_dtype sr
  * pa_decode, bit for bit; a larger bound may change the fp32 summation
  * order (the launch shape depends on max_q_len * num_heads / num_kv_heads).
  *
- *   q             [num_queries][num_heads][head_dim], BF16, 16-byte aligned
+ *   q             [num_queries][num_heads][head_dim], q_dtype (F32 for an
+ *                 F32 cache, else BF16), 16-byte aligned
  *   q_start       int32 [num_seqs + 1], non-decreasing, q_start[0] == 0,
  *                 q_start[num_seqs] == num_queries (device memory)
  *   num_queries   rows of q and out; <= num_seqs * max_q_len
  *   max_q_len     an upper bound of every n_b (sets the launch size)
  *   out           [num_queries][num_heads][head_dim], out_dtype
- *   other arguments as for pa_decode; the cache must be BF16 or I8
- *   (F32 returns PA_ERR_UNSUPPORTED).
+ *   other arguments as for pa_decode; every cache kind is served (F32 on
+ *   the vector ALUs, one wavefront per (query row, head); BF16, I8 and I4
+ *   on the matrix cores).
  * Preconditions (device data): n_b <= max_q_len and n_b <= L; L as for
  * pa_decode.  A sequence whose q_start entries leave [0, num_queries], or
  * with n_b > max_q_len, is skipped (its rows are left as they are); rows of

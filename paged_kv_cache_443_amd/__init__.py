@@ -242,7 +242,7 @@ def decode_multi(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, cache: 
     NQ, Hq, D = q.shape
     if D != cache.head_dim:
         raise ValueError("q head_dim differs from the cache's")
-    _need(q, "q", torch.bfloat16)
+    _need(q, "q", (torch.float32, torch.bfloat16))
     _need(block_tables, "block_tables", torch.int32)
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")

@@ -4,9 +4,11 @@
 // question, step-t equations; block-table walk from the same page's
 // PagedAttention sketch), kept in fp32 end to end: products, online softmax
 // (page "LLM推理优化", section 2.2) and accumulation.  One wavefront per
-// (query head, sequence[, partition]); lane l owns channels l, l + 64.  This
-// path serves fp32 caches (exactness over speed); bf16 and int8 caches use
-// the matrix cores.
+// (query head, sequence[, partition]), or per (query head, query row) for
+// causal multi-query launches (query token i of a sequence's n new tokens
+// sees the positions up to L - n + i: the step-t equations taken for each new
+// token); lane l owns channels l, l + 64.  This path serves fp32 caches
+// (exactness over speed); bf16, int8 and int4 caches use the matrix cores.
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
@@ -21,7 +23,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int D, int BS>
+template <int D, int BS, bool CAUSAL>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeParams p) {
   constexpr int X = 4;
   constexpr int PER = D / 64;
@@ -29,12 +31,34 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeParams p) {
   const int id = blockIdx.x;
   const int hq = id % p.num_heads;
   const int rest = id / p.num_heads;
-  const int b = rest % p.num_seqs;
-  const int part = rest / p.num_seqs;
   const int kvh = hq / p.group;
+  int b, part = 0;
+  size_t row;  // row of q and out (query row x heads + head)
+  int nq = 1, i = 0;
+  if constexpr (CAUSAL) {
+    // query row `rest`: its sequence is the last b with q_start[b] <= rest
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.q_start[mid] <= rest) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    const int qb = p.q_start[b];
+    nq = p.q_start[b + 1] - qb;
+    i = rest - qb;
+    // a sequence whose offsets leave [0, num_queries] or exceed max_q_len is
+    // skipped, as are rows outside it (uniform over the wavefront)
+    if (qb < 0 || nq < 1 || qb + nq > p.num_queries || nq > p.max_q_len || i < 0 || i >= nq) return;
+    row = static_cast<size_t>(rest) * p.num_heads + hq;
+  } else {
+    b = rest % p.num_seqs;
+    part = rest / p.num_seqs;
+    row = static_cast<size_t>(b) * p.num_heads + hq;
+  }
 
   const int L = min(max(p.context_lens[b], 0), p.max_blocks_per_seq * BS);
   int t0 = 0, t1 = L;
+  if constexpr (CAUSAL) t1 = max(0, min(L, L - nq + i + 1));  // positions up to the row's own
   if (p.partition_size > 0) {
     t0 = part * p.partition_size;
     t1 = min(t0 + p.partition_size, L);
@@ -43,7 +67,6 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeParams p) {
   const int32_t *table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float *kpool = static_cast<const float *>(p.k_cache);
   const float *vpool = static_cast<const float *>(p.v_cache);
-  const size_t row = static_cast<size_t>(b) * p.num_heads + hq;
 
   float qv[PER], acc[PER];
 #pragma unroll
@@ -88,9 +111,14 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeParams p) {
 
 template <int D, int BS>
 hipError_t launch_t(const DecodeParams &p, hipStream_t s) {
+  if (p.q_start != nullptr) {  // causal multi-query: one wavefront per (query row, head)
+    const int64_t nwg = static_cast<int64_t>(p.num_heads) * p.num_queries;
+    hipLaunchKernelGGL((decode_f32_kernel<D, BS, true>), dim3(static_cast<uint32_t>(nwg)), dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
   const int64_t nparts = p.partition_size > 0 ? p.max_num_partitions : 1;
   const int64_t nwg = static_cast<int64_t>(p.num_heads) * p.num_seqs * nparts;
-  hipLaunchKernelGGL((decode_f32_kernel<D, BS>), dim3(static_cast<uint32_t>(nwg)), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((decode_f32_kernel<D, BS, false>), dim3(static_cast<uint32_t>(nwg)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

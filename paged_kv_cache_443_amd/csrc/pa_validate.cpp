@@ -95,8 +95,6 @@ pa_status check_split(int32_t partition_size, int32_t max_num_partitions, int32_
 
 pa_status check_multi(const int32_t *q_start, int32_t num_queries, int32_t max_q_len, int32_t num_seqs,
                       int32_t num_heads, const pa_kv_cache *cache) {
-  // the matrix-core path only: a bf16 or int8 cache
-  if (cache->kv_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
   if (num_queries < 0 || max_q_len < 1) return PA_ERR_BAD_SHAPE;
   // every sequence's query rows fit max_q_len, so the rows of all fit the bound
   if (static_cast<int64_t>(num_queries) > static_cast<int64_t>(num_seqs) * max_q_len) return PA_ERR_BAD_SHAPE;

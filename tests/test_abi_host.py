@@ -111,7 +111,7 @@ def test_multi_rejections(L):
     assert _multi(L, c, qs=None) == PA_ERR_NULL_PTR
     assert _multi(L, c, q=None) == PA_ERR_NULL_PTR
     assert _multi(L, c, out=None) == PA_ERR_NULL_PTR
-    assert _multi(L, _cache(kv=PA_F32)) == PA_ERR_UNSUPPORTED  # matrix-core caches only
+    assert _multi(L, _cache(kv=PA_F32)) == PA_ERR_UNSUPPORTED  # bf16 q with an f32 cache
     assert _multi(L, c, mq=0) == PA_ERR_BAD_SHAPE
     assert _multi(L, c, nq=-1) == PA_ERR_BAD_SHAPE
     assert _multi(L, c, nq=13, mq=3) == PA_ERR_BAD_SHAPE  # more rows than num_seqs * max_q_len

@@ -44,6 +44,9 @@ CASES = [
     ("i8", 16, 2, 128, 16, 40, [40, 250, 90, 17]),
     ("i4", 24, 4, 128, 64, 30, [30, 200, 333]),
     ("bf16", 32, 8, 128, 16, 70, [70, 1100, 5, 300]),
+    # fp32 caches (vector ALUs, one wavefront per query row and head)
+    ("f32", 8, 2, 64, 16, 5, [37, 1, 300, 5, 0, 129]),
+    ("f32", 4, 4, 128, 32, 9, [9, 70, 33, 250]),
 ]
 
 
@@ -63,8 +66,9 @@ def test_multi_matches_oracle(case):
     err = max_err(out, want)
     say(f"  max abs err {err:.3e} (tol {TOL[kv]})")
     assert err <= TOL[kv]
-    ob = _multi_gpu(w, cache, q_start, q, mq, torch.bfloat16)
-    assert torch.equal(ob.view(torch.int16).cpu(), bf16_rne_of(out)), "bf16 out must be RNE of the fp32 out"
+    if kv != "f32":  # fp32 caches write fp32 rows only
+        ob = _multi_gpu(w, cache, q_start, q, mq, torch.bfloat16)
+        assert torch.equal(ob.view(torch.int16).cpu(), bf16_rne_of(out)), "bf16 out must be RNE of the fp32 out"
     # a looser max_q_len bound launches more row groups per unit (another
     # split of the tokens between wavefronts): the same values up to fp32
     # summation order
@@ -112,7 +116,7 @@ def test_many_units_match_oracle(case):
     assert torch.equal(ob.view(torch.int16).cpu(), bf16_rne_of(out)), "bf16 out must be RNE of the fp32 out"
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5, "mqa"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5, "mqa"])
 def test_one_new_token_is_decode_bitwise(cfg):
     """With one new token per sequence (max_q_len 1) the multi-query path is
     pa_decode, bit for bit."""
