@@ -50,7 +50,9 @@ Parity status: every function here is pinned by tests that do not re-use
 its own code path (closed forms, invariants, pure-Python brute force, the
 pages' worked block counts); see ``tests/test_oracle_pins.py``.
 """
-from .layout import PagedCache, k_slot, x_per_16b  # noqa: F401
+from .layout import PagedCache  # noqa: F401
+from .storage import k_slot, x_per_16b  # noqa: F401
+from . import storage  # noqa: F401
 from .quant import quantize_int4, quantize_int8, dequantize_int8  # noqa: F401
 from .paged import (  # noqa: F401
     blocks_for,

@@ -10,6 +10,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle
 import paged_kv_cache_443_amd as pa
 from workloads import bf16_bits
 from workloads.device import (DEV, append_tokens, fill_poison, meta, poisoned_cache,  # noqa: F401
@@ -25,18 +26,22 @@ def say(*a):
     sys.stdout.flush()
 
 
+def oracle_pools(oc):
+    """The pools of an oracle-built cache in the library's memory order
+    (bf16 bits, int8 codes, int4 bytes), through the oracle's storage codec."""
+    return oracle.storage.pools(oc)
+
+
 def upload_oracle_cache(oc) -> pa.KVCache:
-    """Device copy of an oracle-built host cache (same layout, same bits)."""
+    """Device copy of an oracle-built host cache (the library's layout, same bits)."""
     kv = oc.kv_dtype
+    kp, vp = oracle_pools(oc)
     if kv == "bf16":
-        k = torch.from_numpy(oc.k.view(np.int16)).to(DEV).view(torch.bfloat16)
-        v = torch.from_numpy(oc.v.view(np.int16)).to(DEV).view(torch.bfloat16)
-    elif kv == "i4":  # the stored bytes, two codes each
-        k = torch.from_numpy(oc.packed_k()).to(DEV)
-        v = torch.from_numpy(oc.packed_v()).to(DEV)
-    else:
-        k = torch.from_numpy(oc.k).to(DEV)
-        v = torch.from_numpy(oc.v).to(DEV)
+        k = torch.from_numpy(kp.view(np.int16)).to(DEV).view(torch.bfloat16)
+        v = torch.from_numpy(vp.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:  # fp32 values, int8 codes, int4 bytes (two codes each)
+        k = torch.from_numpy(kp).to(DEV)
+        v = torch.from_numpy(vp).to(DEV)
     ks = vs = None
     if kv in ("i8", "i4"):
         ks = torch.from_numpy(oc.k_scale).to(DEV)

@@ -230,7 +230,8 @@ def check_cow(decode: DecodeFn) -> None:
 
 
 def check_bruteforce(decode: DecodeFn) -> None:
-    """Against pure-Python scalar loops over the flat pool storage."""
+    """Against pure-Python scalar loops over the flat pool storage (the
+    oracle's logical cache through its storage codec: pins the codec too)."""
     rng = np.random.default_rng(17)
     for kv_dtype, bs, Hq, Hkv, D, lens in [
         ("f32", 16, 4, 4, 64, (7, 16, 33, 40)),
@@ -245,7 +246,8 @@ def check_bruteforce(decode: DecodeFn) -> None:
         got = decode(q, cache, tb, cl, 1.0 / math.sqrt(D))
         ksf = cache.k_scale.ravel().astype(np.float64).tolist() if cache.k_scale is not None else None
         vsf = cache.v_scale.ravel().astype(np.float64).tolist() if cache.v_scale is not None else None
-        want = oracle.decode_bruteforce(q.astype(np.float64).tolist(), cache.k.ravel().tolist(), cache.v.ravel().tolist(),
+        kp, vp = oracle.storage.pools(cache)  # the pools in memory order, as pa.h states it
+        want = oracle.decode_bruteforce(q.astype(np.float64).tolist(), kp.ravel().tolist(), vp.ravel().tolist(),
                                         ksf, vsf, kv_dtype, Hkv, bs, D, tb.tolist(), cl.tolist(), 1.0 / math.sqrt(D))
         _close(got, np.array(want), 1e-12, f"brute force {kv_dtype} bs{bs}")
 

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import paged_kv_cache_443_amd as pa
-from gpu_util import DEV, TOL, download_cache, max_err, say, to_dev_values, upload_oracle_cache
+from gpu_util import DEV, TOL, download_cache, max_err, oracle_pools, say, to_dev_values, upload_oracle_cache
 from workloads import bf16_round
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +30,9 @@ def test_copy_blocks_bit_exact(kv, bs):
     torch.cuda.synchronize()
     oracle.copy_blocks(oc, [p for p in pairs if 0 <= min(p) and max(p) < nb])
     k, v, ks, vs = download_cache(cache)
-    assert np.array_equal(k.view(np.uint8), oc.k.view(np.uint8))
-    assert np.array_equal(v.view(np.uint8), oc.v.view(np.uint8))
+    okp, ovp = oracle_pools(oc)
+    assert np.array_equal(k.view(np.uint8), okp.view(np.uint8))
+    assert np.array_equal(v.view(np.uint8), ovp.view(np.uint8))
     if kv == "i8":
         assert np.array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16))
         assert np.array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16))
@@ -111,6 +112,7 @@ def test_beam_search_with_copy_on_write_matches_oracle():
         want = oracle.decode(q, oc, tables, np.array(lens, np.int32), scale)
         assert max_err(out, want) <= TOL["bf16"], step
     k, v, _, _ = download_cache(cache)
+    okp, ovp = oracle_pools(oc)
     used = sorted({b for t in t_ours for b in t})
-    assert np.array_equal(k[used], oc.k[used]) and np.array_equal(v[used], oc.v[used])
+    assert np.array_equal(k[used], okp[used]) and np.array_equal(v[used], ovp[used])
     assert ours.num_free() == ref.num_free()

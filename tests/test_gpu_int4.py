@@ -8,7 +8,7 @@ import torch
 import oracle
 import paged_kv_cache_443_amd as pa
 from gpu_util import (DEV, TOL, bf16_rne_of, download_cache, fill_poison, gpu_append_tokens, max_err, meta,
-                      poisoned_cache, say, to_dev_values, upload_oracle_cache)
+                      oracle_pools, poisoned_cache, say, to_dev_values, upload_oracle_cache)
 from workloads import bf16_round, make_custom, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -18,8 +18,9 @@ SENTINEL = -123.25
 
 def _same_as_oracle(c: pa.KVCache, oc) -> None:
     k, v, ks, vs = download_cache(c)
-    assert np.array_equal(k, oc.packed_k()), "K bytes"
-    assert np.array_equal(v, oc.packed_v()), "V bytes"
+    okp, ovp = oracle_pools(oc)
+    assert np.array_equal(k, okp), "K bytes"
+    assert np.array_equal(v, ovp), "V bytes"
     assert np.array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16)), "K scales"
     assert np.array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16)), "V scales"
 

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import paged_kv_cache_443_amd as pa
-from gpu_util import DEV, TOL, download_cache, fill_poison, max_err, meta, say, upload_oracle_cache
+from gpu_util import DEV, TOL, download_cache, fill_poison, max_err, meta, oracle_pools, say, upload_oracle_cache
 from workloads import make_custom, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 def _same_bits(c: pa.KVCache, oc) -> bool:
     k, v, ks, vs = download_cache(c)
-    ok = np.array_equal(k.view(np.uint8), oc.k.view(np.uint8)) and np.array_equal(v.view(np.uint8), oc.v.view(np.uint8))
+    okp, ovp = oracle_pools(oc)
+    ok = np.array_equal(k.view(np.uint8), okp.view(np.uint8)) and np.array_equal(v.view(np.uint8), ovp.view(np.uint8))
     if oc.k_scale is not None:
         ok = ok and np.array_equal(ks.view(np.uint16), oc.k_scale.view(np.uint16))
         ok = ok and np.array_equal(vs.view(np.uint16), oc.v_scale.view(np.uint16))

@@ -170,7 +170,7 @@ def test_copy_blocks_moves_exactly_the_blocks(kv_dtype):
 
 def test_copy_blocks_reads_the_pool_before_the_call_and_checks_pairs():
     c = oracle.PagedCache.empty("f32", 4, 1, 16, 16, poison=False)
-    c.k[:] = np.arange(4, dtype=np.float32)[:, None, None, None, None]
+    c.k[:] = np.arange(4, dtype=np.float32)[:, None, None, None]
     with pytest.raises(ValueError):
         oracle.copy_blocks(c, [(0, 1), (1, 2)])  # 1 is both a destination and a source
     with pytest.raises(ValueError):

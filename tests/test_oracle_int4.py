@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import pinlib
-from oracle.layout import pack_nibbles
+from oracle.storage import pack_nibbles, unpack_nibbles
 
 
 def test_int4_golden_rows_and_bytes():
@@ -32,6 +32,7 @@ def test_nibble_packing_round_trips_every_code():
     hi = (packed >> 4).astype(np.int16)
     assert np.array_equal(np.where(lo >= 8, lo - 16, lo), codes[:, 0])
     assert np.array_equal(np.where(hi >= 8, hi - 16, hi), codes[:, 1])
+    assert np.array_equal(unpack_nibbles(pack_nibbles(codes)), codes)
 
 
 def _int4_cache(rng, lens, Hkv=2, D=32, bs=16):
@@ -50,8 +51,9 @@ def test_int4_decode_matches_bruteforce_over_packed_bytes():
     _, _, cache, tb, cl = _int4_cache(rng, lens, Hkv, D, bs)
     q = pinlib.dyadic(rng, (len(lens), Hq, D))
     got = oracle.decode(q, cache, tb, cl, 0.25)
-    want = oracle.decode_bruteforce(q.astype(np.float64).tolist(), cache.packed_k().ravel().tolist(),
-                                    cache.packed_v().ravel().tolist(), cache.k_scale.ravel().tolist(),
+    kp, vp = oracle.storage.pools(cache)  # the stored bytes
+    want = oracle.decode_bruteforce(q.astype(np.float64).tolist(), kp.ravel().tolist(),
+                                    vp.ravel().tolist(), cache.k_scale.ravel().tolist(),
                                     cache.v_scale.ravel().tolist(), "i4", Hkv, bs, D, tb.tolist(), cl.tolist(), 0.25)
     assert np.max(np.abs(got - np.array(want))) < 1e-12
 
@@ -90,7 +92,7 @@ def _pack_high_first(codes):
 
 def test_nibble_order_mutant_is_caught(monkeypatch):
     """Packing the odd element into the low nibble breaks the brute-force pin."""
-    import oracle.layout as layout
-    monkeypatch.setattr(layout, "pack_nibbles", _pack_high_first)
+    import oracle.storage as storage
+    monkeypatch.setattr(storage, "pack_nibbles", _pack_high_first)
     with pytest.raises(AssertionError):
         test_int4_decode_matches_bruteforce_over_packed_bytes()

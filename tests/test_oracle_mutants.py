@@ -71,22 +71,23 @@ def _m_v_channels_reversed(mp):
 
 
 def _m_k_transposed(mp):
+    # channels read as 8-wide vectors transposed (a vector-layout mix-up)
     def k_rows(self, pbs, h, offs):
-        raw = self.k[pbs, h, :, offs, :].transpose(0, 2, 1).reshape(len(pbs), self.D)
+        raw = self.k[pbs, h, offs, :].reshape(len(pbs), self.D // 8, 8).transpose(0, 2, 1).reshape(len(pbs), self.D)
         return self._to_f64(raw, self.k_scale, pbs, h, offs)
     mp.setattr(olayout.PagedCache, "k_rows", k_rows)
 
 
 def _m_v_reads_k(mp):
     def v_rows(self, pbs, h, offs):
-        raw = self.k[pbs, h, :, offs, :].reshape(len(pbs), self.D)
+        raw = self.k[pbs, h, offs, :]
         return self._to_f64(raw, self.k_scale, pbs, h, offs)
     mp.setattr(olayout.PagedCache, "v_rows", v_rows)
 
 
 def _m_scale_from_v(mp):
     def k_rows(self, pbs, h, offs):
-        raw = self.k[pbs, h, :, offs, :].reshape(len(pbs), self.D)
+        raw = self.k[pbs, h, offs, :]
         return self._to_f64(raw, self.v_scale, pbs, h, offs)
     mp.setattr(olayout.PagedCache, "k_rows", k_rows)
 

@@ -44,7 +44,7 @@ def test_single_head_block_base_matches_sketch():
     for kv_dtype in ("f32", "bf16", "i8"):
         nb, bs, D = 5, 16, 64
         c = oracle.PagedCache.empty(kv_dtype, nb, 1, bs, D, poison=False)
-        for pool in (c.k, c.v):
+        for pool in oracle.storage.pools(c):
             flat = pool.reshape(-1)
             for pb in range(nb):
                 region = np.zeros(flat.shape, bool)
@@ -55,7 +55,9 @@ def test_single_head_block_base_matches_sketch():
 
 
 def test_layout_element_positions():
-    """K[pb,h,t,d] and V[pb,h,t,d] land at the documented flat offsets."""
+    """K[pb,h,t,d] and V[pb,h,t,d] sit at [pb, h, t, d] of the oracle's
+    logical cache and, through the storage codec, at the flat offsets pa.h
+    states for the library's pools."""
     rng = np.random.default_rng(3)
     nb, H, bs, D = 3, 2, 16, 32
     c = oracle.PagedCache.empty("f32", nb, H, bs, D, poison=False)
@@ -63,12 +65,41 @@ def test_layout_element_positions():
     V = rng.standard_normal((1, H, D)).astype(np.float32)
     pb, t = 2, 13
     oracle.append(c, K, V, np.array([pb * bs + t]))
+    assert np.array_equal(c.k[pb, :, t, :], K[0]) and np.array_equal(c.v[pb, :, t, :], V[0])
     x = 4
-    kf, vf = c.k.reshape(-1), c.v.reshape(-1)
+    kp, vp = oracle.storage.pools(c)
+    kf, vf = kp.reshape(-1), vp.reshape(-1)
     for h in range(H):
         for d in range(D):
             assert kf[(((pb * H + h) * (D // x) + d // x) * bs + t) * x + d % x] == K[0, h, d]
             assert vf[(((pb * H + h) * (bs // x) + t // x) * D + d) * x + t % x] == V[0, h, d]
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "i8", "i4"])
+def test_storage_codec_round_trips(kv_dtype):
+    """Logical cache -> the library's pools -> logical cache is the identity
+    for every cache kind, and the pools have pa.h's shapes."""
+    rng = np.random.default_rng(31)
+    nb, H, bs, D = 3, 2, 32, 64
+    c = oracle.PagedCache.empty(kv_dtype, nb, H, bs, D, poison=False)
+    if kv_dtype == "f32":
+        c.k[:] = rng.standard_normal(c.k.shape)
+        c.v[:] = rng.standard_normal(c.v.shape)
+    elif kv_dtype == "bf16":
+        c.k[:] = rng.integers(0, 1 << 16, c.k.shape)
+        c.v[:] = rng.integers(0, 1 << 16, c.v.shape)
+    else:
+        lim = 127 if kv_dtype == "i8" else 7
+        c.k[:] = rng.integers(-lim, lim + 1, c.k.shape)
+        c.v[:] = rng.integers(-lim, lim + 1, c.v.shape)
+        c.k_scale[:] = rng.random(c.k_scale.shape)
+        c.v_scale[:] = rng.random(c.v_scale.shape)
+    kp, vp = oracle.storage.pools(c)
+    x = {"f32": 4, "bf16": 8, "i8": 16, "i4": 16}[kv_dtype]
+    w = 8 if kv_dtype == "i4" else x  # int4: 16 codes in 8 bytes
+    assert kp.shape == (nb, H, D // x, bs, w) and vp.shape == (nb, H, bs // x, D, w)
+    back = oracle.storage.from_pools(kv_dtype, kp, vp, c.k_scale, c.v_scale, nb, H, bs, D)
+    assert np.array_equal(back.k, c.k) and np.array_equal(back.v, c.v)
 
 
 def test_bf16_k_slot_order():
@@ -81,11 +112,12 @@ def test_bf16_k_slot_order():
         K = np.full((1, H, D), float(t + 1), np.float32)
         oracle.append(c, K, K, np.array([bs + t]))
     x = 8
+    kflat = oracle.storage.pools(c)[0].reshape(-1)
     for t in range(bs):
         slot = 16 * (t // 16) + want[t % 16]
         for d in range(D):
             flat = (((1 * H + 0) * (D // x) + d // x) * bs + slot) * x + d % x
-            got = oracle.layout.bf16_bits_to_f64(c.k.reshape(-1)[flat])
+            got = oracle.layout.bf16_bits_to_f64(kflat[flat])
             assert got == t + 1, (t, slot, d)
     assert list(oracle.k_slot(np.arange(16), "bf16")) == want
     assert list(oracle.k_slot(np.arange(16), "i8")) == list(range(16))
@@ -145,7 +177,8 @@ def test_oracle_decode_on_tiny_workload_matches_bruteforce():
     w = make_workload(1)
     cache = oracle.build_cache(w)
     got = oracle.decode(w.q, cache, w.block_tables, w.context_lens, w.spec.scale)
-    want = oracle.decode_bruteforce(w.q.astype(np.float64).tolist(), cache.k.ravel().tolist(), cache.v.ravel().tolist(),
+    kp, vp = oracle.storage.pools(cache)
+    want = oracle.decode_bruteforce(w.q.astype(np.float64).tolist(), kp.ravel().tolist(), vp.ravel().tolist(),
                                     None, None, "f32", w.spec.Hkv, w.spec.bs, w.spec.D, w.block_tables.tolist(),
                                     w.context_lens.tolist(), w.spec.scale)
     assert np.max(np.abs(got - np.array(want))) < 1e-12
@@ -201,8 +234,9 @@ def test_decode_multi_pins():
             rows_q.append(q[qs[b] + i].astype(np.float64).tolist())
             rows_tb.append(tb[b].tolist())
             rows_len.append(L - nq[b] + i + 1)
-    brute = oracle.decode_bruteforce([[r[h] for h in range(Hq)] for r in rows_q], cache.k.ravel().tolist(),
-                                     cache.v.ravel().tolist(), None, None, "f32", Hkv, bs, D, rows_tb, rows_len,
+    kp, vp = oracle.storage.pools(cache)
+    brute = oracle.decode_bruteforce([[r[h] for h in range(Hq)] for r in rows_q], kp.ravel().tolist(),
+                                     vp.ravel().tolist(), None, None, "f32", Hkv, bs, D, rows_tb, rows_len,
                                      scale)
     assert np.max(np.abs(got - np.array(brute))) <= 1e-12
     # causality: changing a key after a row's position does not change that row
