@@ -407,8 +407,7 @@ __device__ __forceinline__ void softmax(State<KV, D> &st, Scores<KV, D> &S, cons
       mloc = fmaxf(mloc, sv);
     }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  mloc = max_over_rows(mloc);
   const float m_new = fmaxf(st.m_run, mloc);
   // The exponentials are taken against a reference (st.m_run) that moves only
   // when a chunk's maximum passes it by more than kLazyLog2, so every
@@ -919,8 +918,7 @@ __device__ __forceinline__ void softmax_fold(State<kBf16, D> &st, f32x4 &lsum, S
       mloc = fmaxf(mloc, sv);
     }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  mloc = max_over_rows(mloc);
   const float mc = mloc == -INFINITY ? -INFINITY : mloc * c;
   const float m_new = fmaxf(st.m_run, mc);
   const bool move = m_new > st.m_run + kLazyLog2;
@@ -1201,10 +1199,10 @@ __device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG) {
 // through LDS one row group at a time.  Causal rows (query token r / G of the
 // sequence's nq new tokens, head r % G) mask per lane; chunks that end before
 // the unit's first row's position need no mask.  Eight wavefronts per unit,
-// one work-group per CU: head_dim 128 with block size 16 takes 233 / 238
-// (bf16, single token / causal rows) and 225 / 243 (int4) VGPRs, no spills;
-// int8 takes 254 (at block size 32: 256 and a 16-byte spill per lane) and
-// serves single tokens only (with causal rows it spilled more).
+// one work-group per CU: head_dim 128 with block size 16 takes 225 / 234
+// (bf16, single token / causal rows) and 221 / 238 (int4) VGPRs, no spills;
+// int8 takes 248-253 and serves single tokens only (with causal rows it
+// spills 12-76 bytes per lane).
 
 // QK of both row groups off each converted K fragment (converted once).
 template <int KV, int D>

@@ -42,6 +42,20 @@ __host__ __device__ __forceinline__ int bf16_k_slot(int t) { return (t & ~12) | 
 // accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Maximum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
+// 16-lane rows of the wavefront; a matrix-core output row's lane groups j).
+// gfx950's row-swap instructions exchange the halves (permlane32_swap) and
+// then the odd and even rows (permlane16_swap) of a register in the vector
+// ALU; with both operands the same value, each lane gets its partner's value
+// in one of the two results.  An exact maximum, so the order does not matter;
+// no LDS permute round trip.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // 2^x on the transcendental unit (inputs here are <= 0 or -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

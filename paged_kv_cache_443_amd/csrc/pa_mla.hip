@@ -228,8 +228,7 @@ __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, con
       sv[i] = cs + 16 * w + 4 * j + i < t1 ? (a[i] + b[i]) * scale_log2 : -INFINITY;
       mx = fmaxf(mx, sv[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_rows(mx);
     if (j == 0) sm.gmax[w * 16 + m] = mx;
   }
   lds_barrier();
