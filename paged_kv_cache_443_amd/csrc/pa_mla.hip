@@ -38,9 +38,10 @@
 //       maximum of each head from LDS (the same value in every wave); then
 //       it writes P as bf16 hi + lo parts to LDS and keeps the running sums.
 //   PV  O^T[dim][head] += C^T[dim][token] P^T[token][head]   wave w: latent
-//       dims 128w .. 128w + 127 over all 64 tokens.  A = C^T (the staged
-//       rows read down a column as 32-bit words, the wanted halves picked
-//       with a byte permute), B = P as bf16 hi + lo from LDS.
+//       dims 128w .. 128w + 127 over all 64 tokens.  A = C^T, read down the
+//       staged rows' columns with gfx950's transposing LDS read
+//       (ds_read_b64_tr_b16, two per operand), B = P as bf16 hi + lo from
+//       LDS.
 // Every wave rescales with the same maxima, so the four dimension slices
 // need no merge: each wave writes its own 128 dims of the partial output.
 // The latent rows of the next chunk are in flight in VGPRs while one chunk
@@ -80,6 +81,19 @@ constexpr size_t kMlaFixedLds = kRowsBytes + kScoreBytes + static_cast<size_t>(2
 
 __host__ __device__ constexpr size_t mla_lds_bytes(int tbl_window, int num_seqs) {
   return kMlaFixedLds + static_cast<size_t>(tbl_window) * 4 + static_cast<size_t>(num_seqs + 1) * 4;
+}
+
+// gfx950's transposing LDS read of 16-bit elements: within each 16-lane
+// group, every lane names 8 bytes (4 elements) and lane t = 4a + b receives
+// element b of the lanes a, a + 4, a + 8 and a + 12, in that order (the
+// mapping was measured with a probe kernel).  When lane s of a group points
+// at 4 consecutive dims d0 + 4 (s % 4) .. of staged row r0 + s / 4, lane t
+// receives dim d0 + t of rows r0 .. r0 + 3: four consecutive tokens of one
+// dim, half of a matrix-core A operand lane for the PV product.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+__device__ __forceinline__ v4s lds_read_tr16(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p));
 }
 
 __device__ __forceinline__ bf16x8 bf16x8_of(const float *x) {
@@ -263,21 +277,19 @@ __device__ __forceinline__ void mla_compute(MlaState &st, const MlaSmem &sm, con
     const bf16x8 phi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sm.ph + m * PPAD + 32 * ks + 8 * j));
     const bf16x8 plo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sm.pl + m * PPAD + 32 * ks + 8 * j));
     // A = C^T: lane (dim 128 w + 16 n + m, j) needs rows 32 ks + 8 j + e of its
-    // column.  It reads the 32-bit word holding its dim and its neighbour
-    // (no 16-bit loads merging into one register, which serialise) and keeps
-    // its half; all rows of the k-step share the swizzle 2 j.
-    const unsigned char *col = sm.rows + static_cast<size_t>(32 * ks + 8 * j) * ROW + ((m & 7) >> 1) * 4;
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two words
+    // column, e = 0 .. 7.  Two transposing reads: this lane points at row
+    // 32 ks + 8 j + m / 4 (then 4 rows further), dims 128 w + 16 n + 4 (m % 4)
+    // .. + 3 (8 bytes of a 16-byte vector); all rows of the k-step share the
+    // swizzle 2 j.  (Before: eight 32-bit reads down the column and four byte
+    // permutes per operand; the whole decode 161.5 -> 159.1 us, bit for bit
+    // the same.)
+    const unsigned char *trow = sm.rows + static_cast<size_t>(32 * ks + 8 * j + (m >> 2)) * ROW + 8 * (m & 1);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const int v = (16 * w + 2 * n + (m >> 3)) ^ (2 * j);
-      uint32_t wd[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wd[e] = *reinterpret_cast<const uint32_t *>(col + static_cast<size_t>(e) * ROW + v * 16);
-      u32x4 pk;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_perm(wd[2 * k + 1], wd[2 * k], sel);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, pk);
+      const int v = (16 * w + 2 * n + ((m & 3) >> 1)) ^ (2 * j);
+      const v4s t0 = lds_read_tr16(trow + v * 16);
+      const v4s t1 = lds_read_tr16(trow + 4 * ROW + v * 16);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.acc[n], 0, 0, 0);
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.acc[n], 0, 0, 0);
     }
