@@ -447,56 +447,65 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ml
   }
 }
 
-// ---- 3. merge the partitions and up-project ------------------------------------
-// Work-group: head h, 4 sequences, 256 threads (four sequences rather than
-// eight: twice the work-groups, measured 164.3 -> 162.3 us for the whole
-// decode on the benchmark batch).
-//   merge: thread (sequence bb = t / 64, channels 8 (t % 64) ..): o_lat =
+// ---- 3. merge the partitions and up-project, on the matrix cores -----------------
+// Work-group: head h, kUmSeqs sequences, 256 threads.
+//   merge: thread (sequence bb = t / 32, channels 16 (t % 32) ..): o_lat =
 //          sum_p e^{lse_p - M} o_p / sum_p e^{lse_p - M} (partitions in
-//          order), kept in LDS as [channel][sequence];
-//   up:    out[b][h][d] = sum_c o_lat[c] W_uv[c][h * DH + d], W_uv's rows
-//          staged in LDS 64 at a time (coalesced loads of the next rows in
-//          flight while the current ones are used); thread (d, slice) sums
-//          every SL-th channel, the SL slices added in slice order.
-constexpr int kUpSeqs = 4;
-static_assert(kUpSeqs % 4 == 0, "o_lat is read four sequences per 16-byte vector");
-constexpr int kUpThreads = 256;
-constexpr int kUpRows = 64;  // W_uv rows per staged chunk
+//          order), kept in LDS as bf16 hi + lo rows (the A operand: rows of
+//          sequences; rows kUmSeqs .. 15 zero).
+//   up:    out[b][h][:] = o_lat W_uv,h on 16x16x32 MFMAs: wave w takes the
+//          output dims 16 (NTW w + nt) ..; W_uv's rows staged in LDS 64 at a
+//          time (the next chunk's loads in flight), its columns read with the
+//          transposing LDS read (the B operand: 8 channels of one dim per lane).
+// (Before: the up-projection on the vector ALUs, W_uv read from LDS one
+// element per product: 19.9 us on the benchmark batch, its waves held at the
+// staging barriers; now the whole decode 158.6 -> 152.2 us.)
+constexpr int kUmSeqs = 8;
+constexpr int kUmThreads = 256;
+constexpr int kUmRows = 64;
+constexpr int kOPad = DC + 8;  // bf16 per staged o_lat row
 
 template <int DH>
-__global__ __launch_bounds__(kUpThreads) void mla_merge_up_kernel(MlaParams p) {
-  constexpr int SL = kUpThreads / DH;
-  constexpr int VPRW = DH / 8;                              // 16-byte vectors per W_uv row slice
-  constexpr int WV = kUpRows * VPRW / kUpThreads;           // vectors per thread per chunk
-  static_assert(WV * kUpThreads == kUpRows * VPRW, "whole chunks");
-  __shared__ __align__(16) float olT[DC][kUpSeqs];
-  __shared__ __align__(16) uint16_t wl[2][kUpRows][DH];
-  __shared__ float red[SL][kUpSeqs][DH + 1];
+__global__ __launch_bounds__(kUmThreads) void mla_merge_up_kernel(MlaParams p) {
+  constexpr int WROW = DH + 16;                       // bf16 per staged W_uv row (32 bytes of padding)
+  constexpr int VPW = DH / 8;                         // 16-byte vectors per W_uv row slice
+  constexpr int WV = kUmRows * VPW / kUmThreads;      // vectors per thread per chunk
+  constexpr int NTW = DH / 64;                        // 16-dim output tiles per wave
+  static_assert(WV * kUmThreads == kUmRows * VPW && NTW >= 1, "shapes");
+  __shared__ __align__(16) uint16_t oh[16][kOPad];
+  __shared__ __align__(16) uint16_t ol[16][kOPad];
+  __shared__ __align__(16) uint16_t wl[2][kUmRows][WROW];
   const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(p.num_heads));
-  const int b0 = static_cast<int>(blockIdx.x / static_cast<uint32_t>(p.num_heads)) * kUpSeqs;
-  const int nb = min(kUpSeqs, p.num_seqs - b0);
+  const int b0 = static_cast<int>(blockIdx.x / static_cast<uint32_t>(p.num_heads)) * kUmSeqs;
+  const int nb = min(kUmSeqs, p.num_seqs - b0);
   const int Lmax = p.max_blocks_per_seq * p.block_size;
   const int t = threadIdx.x;
-  const size_t wstride = static_cast<size_t>(p.num_heads) * DH;  // W_uv row length (elements)
+  const int lane = t & 63, w = t >> 6, m = lane & 15, j = lane >> 4;
+  const size_t wstride = static_cast<size_t>(p.num_heads) * DH;
   const uint16_t *wbase = p.w_uv + static_cast<size_t>(h) * DH;
 
-  // the first W_uv chunk's loads go out before the merge
   u32x4 wr[WV];
   auto issue_w = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < WV; ++i) {
-      const int v = t + kUpThreads * i;
-      wr[i] = *reinterpret_cast<const u32x4 *>(wbase + static_cast<size_t>(c0 + v / VPRW) * wstride + (v % VPRW) * 8);
+      const int v = t + kUmThreads * i;
+      wr[i] = *reinterpret_cast<const u32x4 *>(wbase + static_cast<size_t>(c0 + v / VPW) * wstride + (v % VPW) * 8);
+    }
+  };
+  auto stage_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int v = t + kUmThreads * i;
+      *reinterpret_cast<u32x4 *>(&wl[buf][v / VPW][(v % VPW) * 8]) = wr[i];
     }
   };
   issue_w(0);
 
   {
-    constexpr int CPT = DC * kUpSeqs / kUpThreads;  // channels per thread: 8
-    const int bb = t / (DC / CPT), c0 = (t % (DC / CPT)) * CPT;
-    float acc[CPT];
+    const int bb = t / 32, c0 = (t % 32) * 16;
+    float acc[16];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     float l = 0.f;
     if (bb < nb) {
       const int b = b0 + bb;
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(kUpThreads) void mla_merge_up_kernel(MlaParams p) {
         l += wt;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part_out + (row + q) * DC + c0);
 #pragma unroll
-        for (int v = 0; v < CPT / 4; ++v) {
+        for (int v = 0; v < 4; ++v) {
           const f32x4 x = src[v];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[4 * v + i] += wt * x[i];
@@ -519,49 +528,70 @@ __global__ __launch_bounds__(kUpThreads) void mla_merge_up_kernel(MlaParams p) {
       }
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;  // L = 0: a zero row
+    u32x4 hv[2], lv[2];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) olT[c0 + i][bb] = acc[i] * inv;
-  }
-
-  const int d = t % DH, sl = t / DH;
-  float acc[kUpSeqs];
-#pragma unroll
-  for (int bb = 0; bb < kUpSeqs; ++bb) acc[bb] = 0.f;
-  for (int k = 0; k < DC / kUpRows; ++k) {
-    const int buf = k & 1;
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int v = t + kUpThreads * i;
-      *reinterpret_cast<u32x4 *>(&wl[buf][v / VPRW][(v % VPRW) * 8]) = wr[i];
+    for (int e = 0; e < 16; e += 2) {
+      const float o0 = acc[e] * inv, o1 = acc[e + 1] * inv;
+      const __bf16 h0 = static_cast<__bf16>(o0), h1 = static_cast<__bf16>(o1);
+      const __bf16 l0 = static_cast<__bf16>(o0 - static_cast<float>(h0));
+      const __bf16 l1 = static_cast<__bf16>(o1 - static_cast<float>(h1));
+      hv[e >> 3][(e >> 1) & 3] = __builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+      lv[e >> 3][(e >> 1) & 3] = __builtin_bit_cast(uint16_t, l0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
     }
-    if (k + 1 < DC / kUpRows) issue_w((k + 1) * kUpRows);
-    lds_barrier();  // chunk k of W_uv (and, the first time, o_lat) staged
-#pragma unroll 4
-    for (int r = sl; r < kUpRows; r += SL) {
-      const float wf = bf16_bits_to_float(wl[buf][r][d]);
-      const f32x4 *o = reinterpret_cast<const f32x4 *>(&olT[k * kUpRows + r][0]);
 #pragma unroll
-      for (int v = 0; v < kUpSeqs / 4; ++v) {
-        const f32x4 x = o[v];
+    for (int k = 0; k < 2; ++k) {
+      *reinterpret_cast<u32x4 *>(&oh[bb][c0 + 8 * k]) = hv[k];
+      *reinterpret_cast<u32x4 *>(&ol[bb][c0 + 8 * k]) = lv[k];
+      // the padding rows of the A operand
+      *reinterpret_cast<u32x4 *>(&oh[kUmSeqs + bb][c0 + 8 * k]) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(&ol[kUmSeqs + bb][c0 + 8 * k]) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  static_assert(kUmSeqs == 8, "the padding rows are written by the merge threads");
+  stage_w(0);
+
+  f32x4 acc[NTW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[4 * v + i] += x[i] * wf;
+  for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int NCH = DC / kUmRows;
+  for (int k = 0; k < NCH; ++k) {
+    const int buf = k & 1;
+    if (k + 1 < NCH) issue_w((k + 1) * kUmRows);
+    lds_barrier();  // chunk k staged (and, the first time, the o_lat rows)
+#pragma unroll
+    for (int ks = 0; ks < kUmRows / 32; ++ks) {
+      const int cb = k * kUmRows + 32 * ks;
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&oh[m][cb + 8 * j]));
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ol[m][cb + 8 * j]));
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int d0 = 16 * (NTW * w + nt);
+        const unsigned char *src =
+            reinterpret_cast<const unsigned char *>(&wl[buf][32 * ks + 8 * j + (m >> 2)][d0 + 4 * (m & 3)]);
+        const v4s t0 = lds_read_tr16(src);
+        const v4s t1 = lds_read_tr16(src + 4 * WROW * 2);
+        const bf16x8 bw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[nt], 0, 0, 0);
       }
     }
-    // buffer buf is rewritten two chunks later, after the next barrier
+    if (k + 1 < NCH) stage_w(buf ^ 1);  // its readers (chunk k - 1) passed this chunk's barrier
   }
+  // lane (dim m of the tile, j) holds sequences 4 j .. 4 j + 3
 #pragma unroll
-  for (int bb = 0; bb < kUpSeqs; ++bb) red[sl][bb][d] = acc[bb];
-  __syncthreads();
-  for (int i = t; i < nb * DH; i += kUpThreads) {
-    const int bb = i / DH, dd = i % DH;
-    float o = 0.f;
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int d = 16 * (NTW * w + nt) + m;
 #pragma unroll
-    for (int v = 0; v < SL; ++v) o += red[v][bb][dd];
-    const size_t idx = (static_cast<size_t>(b0 + bb) * p.num_heads + h) * DH + dd;
-    if (p.out_bf16)
-      static_cast<uint16_t *>(p.out)[idx] = float_to_bf16_bits(o);
-    else
-      static_cast<float *>(p.out)[idx] = o;
+    for (int i = 0; i < 4; ++i) {
+      const int bb = 4 * j + i;
+      if (bb < nb) {
+        const size_t idx = (static_cast<size_t>(b0 + bb) * p.num_heads + h) * DH + d;
+        if (p.out_bf16)
+          static_cast<uint16_t *>(p.out)[idx] = float_to_bf16_bits(acc[nt][i]);
+        else
+          static_cast<float *>(p.out)[idx] = acc[nt][i];
+      }
+    }
   }
 }
 
@@ -608,9 +638,9 @@ hipError_t launch_dh(const MlaParams &p, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const uint32_t ugroups = static_cast<uint32_t>((p.num_seqs + kUpSeqs - 1) / kUpSeqs);
-  hipLaunchKernelGGL(mla_merge_up_kernel<DH>, dim3(ugroups * static_cast<uint32_t>(p.num_heads)), dim3(kUpThreads), 0,
-                     s, p);
+  const uint32_t ugroups = static_cast<uint32_t>((p.num_seqs + kUmSeqs - 1) / kUmSeqs);
+  hipLaunchKernelGGL(mla_merge_up_kernel<DH>, dim3(ugroups * static_cast<uint32_t>(p.num_heads)),
+                     dim3(kUmThreads), 0, s, p);
   return hipGetLastError();
 }
 
