@@ -106,16 +106,24 @@ __device__ __forceinline__ bf16x8 bf16x8_of(const float *x) {
 // ---- 1. absorb: q_lat[b][h][c] = sum_d W_uk[c][h * DH + d] q[b][h][d] --------
 // On the matrix cores: Q_lat^T[c][b] = W_uk_h[c][:] . Q[b][:] with the 16
 // sequences of a work-group as the N dimension (bf16 operands, exact
-// products, fp32 sums).  Work-group: head h, 16 sequences, 8 wavefronts;
-// wavefront w takes latent channels 64w .. 64w + 63 (four 16-row tiles).
+// products, fp32 sums).  Work-group: head h, 16 sequences, half the latent
+// channels (4 wavefronts); wavefront w, counted over both halves, takes
+// latent channels 64w .. 64w + 63 (four 16-row tiles).
 constexpr int kAbsorbSeqs = 16;
+// The latent channels of a (head, 16 sequences) are split over two four-wave
+// work-groups, so that the launch covers every CU (the same values; 7.3 ->
+// 5.3 us on the benchmark batch, the whole decode 152.1 -> 150.5 us).
+constexpr int kAbsorbParts = 2;
+constexpr int kAbsorbThreads = DC / kAbsorbParts;
 
 template <int DH>
-__global__ __launch_bounds__(DC) void mla_absorb_kernel(MlaParams p) {
+__global__ __launch_bounds__(kAbsorbThreads) void mla_absorb_kernel(MlaParams p) {
   constexpr int KS = DH / 32;  // k-steps over head_dim
-  const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(p.num_heads));
-  const int b0 = static_cast<int>(blockIdx.x / static_cast<uint32_t>(p.num_heads)) * kAbsorbSeqs;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t id = blockIdx.x / kAbsorbParts;
+  const int part = static_cast<int>(blockIdx.x % kAbsorbParts);
+  const int h = static_cast<int>(id % static_cast<uint32_t>(p.num_heads));
+  const int b0 = static_cast<int>(id / static_cast<uint32_t>(p.num_heads)) * kAbsorbSeqs;
+  const int lane = threadIdx.x & 63, w = static_cast<int>(threadIdx.x >> 6) + part * (kAbsorbThreads / 64);
   const int m = lane & 15, j = lane >> 4;
   // B operand: lane (sequence m, j) holds q[b0 + m][h][32 s + 8 j ..]
   bf16x8 qb[KS];
@@ -628,7 +636,8 @@ hipError_t launch_attn(const MlaParams &p, hipStream_t s) {
 template <int DH>
 hipError_t launch_dh(const MlaParams &p, hipStream_t s) {
   const uint32_t groups = static_cast<uint32_t>((p.num_seqs + kAbsorbSeqs - 1) / kAbsorbSeqs);
-  hipLaunchKernelGGL(mla_absorb_kernel<DH>, dim3(groups * static_cast<uint32_t>(p.num_heads)), dim3(DC), 0, s, p);
+  hipLaunchKernelGGL(mla_absorb_kernel<DH>, dim3(groups * static_cast<uint32_t>(p.num_heads) * kAbsorbParts),
+                     dim3(kAbsorbThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (p.block_size) {
