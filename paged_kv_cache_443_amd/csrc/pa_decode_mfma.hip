@@ -968,10 +968,12 @@ __device__ __forceinline__ void pv_fold(State<kBf16, D> &st, f32x4 &lsum, VBuf<k
   lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, lsum, 0, 0, 0);
 }
 
+// One chunk of an int8 / int4 wide unit: QK, then each row group's softmax and PV.
 template <int KV, int D, int BS, bool TAIL, bool REFILL, int RW>
 __device__ __forceinline__ void consume_wide(State<KV, D> (&st)[RW], f32x4 (&lsum)[RW], KBuf<KV, D> &kb,
                                              VBuf<KV, D> &vb, const Ctx<KV, D, BS> &x, const QOp<KV, D> (&qop)[RW],
                                              const int (&t1r)[RW], int cs, int cn, Ids idn, float scale_log2) {
+  static_assert(KV != kBf16, "bf16 wide units take consume_pipelined");
   using T = Tile<KV, D>;
   Scores<KV, D> S[RW];
 #pragma unroll
@@ -981,20 +983,11 @@ __device__ __forceinline__ void consume_wide(State<KV, D> (&st)[RW], f32x4 (&lsu
     issue_k<false>(kb, x, cn, idn);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (KV == kBf16) {
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      Probs<KV, D> P;
-      softmax_fold<D, TAIL>(st[r], lsum[r], S[r], P, cs + T::TPL * x.j, t1r[r], scale_log2);
-      pv_fold<D, TAIL>(st[r], lsum[r], vb, P, cs + T::TPL * x.j, x.t1);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      Probs<KV, D> P;
-      softmax<KV, D, TAIL, true>(st[r], S[r], vb, P, cs + T::TPL * x.j, t1r[r], scale_log2, qop[r].bias);
-      pv_update<KV, D, TAIL, false>(st[r], vb, P, cs + T::TPL * x.j, x.t1);
-    }
+  for (int r = 0; r < RW; ++r) {
+    Probs<KV, D> P;
+    softmax<KV, D, TAIL, true>(st[r], S[r], vb, P, cs + T::TPL * x.j, t1r[r], scale_log2, qop[r].bias);
+    pv_update<KV, D, TAIL, false>(st[r], vb, P, cs + T::TPL * x.j, x.t1);
   }
   if constexpr (REFILL) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1003,7 +996,49 @@ __device__ __forceinline__ void consume_wide(State<KV, D> (&st)[RW], f32x4 (&lsu
   }
 }
 
-// n >= 1 consecutive chunks from c0, one in flight while the previous one is computed.
+// bf16 wide units, software-pipelined over chunks: on entry S holds chunk
+// cs's scores and kb holds K of the next chunk cn.  Chunk cn's QK products
+// are issued before chunk cs's softmax and PV (they share no registers), so
+// a wavefront's softmax never waits on the matrix-core results of its own
+// chunk; K of chunk cnn (two ahead) then refills kb, V of cn refills vb once
+// chunk cs's PV has read it.  Every product and its order is the same as
+// in a chunk-by-chunk loop (QK, softmax, PV of one chunk, then the next), so
+// the results are too, bit for bit.  NEXT: a chunk cn follows; REFILL: a
+// chunk cnn follows it.
+template <int D, int BS, bool TAIL, bool NEXT, bool REFILL, int RW>
+__device__ __forceinline__ void consume_pipelined(State<kBf16, D> (&st)[RW], f32x4 (&lsum)[RW],
+                                                  Scores<kBf16, D> (&S)[RW], KBuf<kBf16, D> &kb, VBuf<kBf16, D> &vb,
+                                                  const Ctx<kBf16, D, BS> &x, const QOp<kBf16, D> (&qop)[RW],
+                                                  const int (&t1r)[RW], int cs, int cn, Ids idn, int cnn, Ids idnn,
+                                                  float scale_log2) {
+  using T = Tile<kBf16, D>;
+  Scores<kBf16, D> Sn[RW];
+  if constexpr (NEXT) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) qk<kBf16, D>(Sn[r], kb, qop[r]);
+    if constexpr (REFILL) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_k<false>(kb, x, cnn, idnn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    Probs<kBf16, D> P;
+    softmax_fold<D, TAIL>(st[r], lsum[r], S[r], P, cs + T::TPL * x.j, t1r[r], scale_log2);
+    pv_fold<D, TAIL>(st[r], lsum[r], vb, P, cs + T::TPL * x.j, x.t1);
+  }
+  if constexpr (NEXT) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_v<false>(vb, x, cn, idn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) S[r] = Sn[r];
+  }
+}
+
+// n >= 1 consecutive chunks from c0, the next one's loads in flight while
+// the current one is computed (bf16: pipelined as above).
 template <int KV, int D, int BS, int RW>
 __device__ __forceinline__ void stream_wide(State<KV, D> (&st)[RW], f32x4 (&lsum)[RW], const Ctx<KV, D, BS> &x,
                                             const QOp<KV, D> (&qop)[RW], const int (&t1r)[RW], int c0, int n,
@@ -1015,15 +1050,51 @@ __device__ __forceinline__ void stream_wide(State<KV, D> (&st)[RW], f32x4 (&lsum
   const Ids ids = read_ids(x, cs);
   issue_k<false>(kb, x, cs, ids);
   issue_v<false>(vb, x, cs, ids);
-  for (int k = 0; k + 1 < n; ++k) {
-    const int cn = cs + CT;
-    if (cs + CT > x.t1_min)  // the wavefront's first row cannot see all of this chunk
-      consume_wide<KV, D, BS, true, true, RW>(st, lsum, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), scale_log2);
-    else
-      consume_wide<KV, D, BS, false, true, RW>(st, lsum, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), scale_log2);
-    cs = cn;
+  if constexpr (KV == kBf16) {
+    Scores<KV, D> S[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) qk<KV, D>(S[r], kb, qop[r]);
+    Ids idn{0, 0};  // block ids of chunk cs + CT, whose K is in flight
+    if (n > 1) {
+      idn = read_ids(x, cs + CT);
+      issue_k<false>(kb, x, cs + CT, idn);
+    }
+    for (int k = 0; k + 1 < n; ++k) {
+      const int cn = cs + CT;
+      const int cnn = cn + CT;
+      const bool tail = cs + CT > x.t1_min;  // the wavefront's first row cannot see all of chunk cs
+      if (k + 2 < n) {
+        const Ids idnn = read_ids(x, cnn);
+        if (tail)
+          consume_pipelined<D, BS, true, true, true, RW>(st, lsum, S, kb, vb, x, qop, t1r, cs, cn, idn, cnn, idnn,
+                                                         scale_log2);
+        else
+          consume_pipelined<D, BS, false, true, true, RW>(st, lsum, S, kb, vb, x, qop, t1r, cs, cn, idn, cnn, idnn,
+                                                          scale_log2);
+        idn = idnn;
+      } else {
+        if (tail)
+          consume_pipelined<D, BS, true, true, false, RW>(st, lsum, S, kb, vb, x, qop, t1r, cs, cn, idn, 0,
+                                                          Ids{0, 0}, scale_log2);
+        else
+          consume_pipelined<D, BS, false, true, false, RW>(st, lsum, S, kb, vb, x, qop, t1r, cs, cn, idn, 0,
+                                                           Ids{0, 0}, scale_log2);
+      }
+      cs = cn;
+    }
+    consume_pipelined<D, BS, true, false, false, RW>(st, lsum, S, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, 0, Ids{0, 0},
+                                                     scale_log2);
+  } else {
+    for (int k = 0; k + 1 < n; ++k) {
+      const int cn = cs + CT;
+      if (cs + CT > x.t1_min)  // the wavefront's first row cannot see all of this chunk
+        consume_wide<KV, D, BS, true, true, RW>(st, lsum, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), scale_log2);
+      else
+        consume_wide<KV, D, BS, false, true, RW>(st, lsum, kb, vb, x, qop, t1r, cs, cn, read_ids(x, cn), scale_log2);
+      cs = cn;
+    }
+    consume_wide<KV, D, BS, true, false, RW>(st, lsum, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, scale_log2);
   }
-  consume_wide<KV, D, BS, true, false, RW>(st, lsum, kb, vb, x, qop, t1r, cs, 0, Ids{0, 0}, scale_log2);
 }
 
 // One wide unit: sequence b, kv head hx / head_groups, row groups
