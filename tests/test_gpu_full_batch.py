@@ -65,6 +65,7 @@ def test_full_batch_step_matches_oracle(case):
 WIDE = [
     ("bf16", 40, 40, 2048, 512, 8, 16),
     ("bf16", 64, 8, 1500, 300, 8, 32),
+    ("bf16", 32, 8, 1100, 200, 8, 64),
     ("i8", 32, 8, 2048, 256, 8, 16),
     ("i4", 32, 8, 1024, 128, 16, 64),
 ]
