@@ -1237,13 +1237,24 @@ __device__ __forceinline__ void run_wide_unit(const DecodeParams &p, int32_t *tb
   }
 }
 
-// bf16: at least two wavefronts per SIMD (two four-wave work-groups per CU)
+__device__ __forceinline__ int xcd_grouped_unit(int id, int NP, int HG);
+
+// bf16: at least two wavefronts per SIMD (two four-wave work-groups per CU).
+// With eight or more units per (sequence, kv head), work-groups in index
+// order would put a pair's units on every XCD and each XCD's L2 would fetch
+// all of its lines; they are grouped onto one XCD instead (xcd_grouped_unit;
+// measured on 512-token chunks, 70B-shaped heads, 32 units per pair: 323.2 ->
+// 314.7 us; grouping the 4 units per pair of 13B-shaped heads too measured
+// 239.5 -> 241.7 us, so those keep index order).  Only the unit -> work-group assignment moves: same results.
 template <int KV, int D, int BS, int NW, int RW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV == kBf16 ? 2 : 1)))
 void decode_wide_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HX = p.num_kv_heads * p.head_groups;
-  run_wide_unit<KV, D, BS, NW, RW>(p, reinterpret_cast<int32_t *>(smem), blockIdx.x / HX, blockIdx.x % HX);
+  const int u = p.head_groups >= 8
+                    ? xcd_grouped_unit(static_cast<int>(blockIdx.x), p.num_seqs * p.num_kv_heads, p.head_groups)
+                    : static_cast<int>(blockIdx.x);
+  run_wide_unit<KV, D, BS, NW, RW>(p, reinterpret_cast<int32_t *>(smem), u / HX, u % HX);
 }
 
 // Several units per (sequence, kv head) (more query-head groups than one
