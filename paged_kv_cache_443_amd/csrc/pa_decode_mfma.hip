@@ -1553,8 +1553,9 @@ __device__ __forceinline__ void run_unit_rw(const DecodeParams &p, const Smem &s
   }
 }
 
+// at least two wavefronts per SIMD (two four-wave work-groups per CU)
 template <int KV, int D, int BS, int NW, bool CAUSAL, bool NT>
-__global__ __launch_bounds__(NW * 64) void decode_rw_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_rw_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Smem sm = carve<D, NW>(smem, p.tbl_window, 16);
   const int HX = p.num_kv_heads * p.head_groups;
@@ -1826,6 +1827,32 @@ bool use_wide(const DecodeParams &p, hipError_t &e) {
   return units >= cus;
 }
 
+// Two-group units (decode_rw_kernel) with NWR wavefronts each; q.head_groups
+// is the number of units per kv head.
+template <int KV, int D, int BS, int NWR, bool CAUSAL>
+hipError_t launch_rw(const DecodeParams &q, hipStream_t s) {
+  // several units per (sequence, kv head) read the same lines, side by side
+  // on one XCD: ordinary loads, so that all but the first read hit its L2
+  // (64 query heads on one kv head, 128 x 4096 tokens: HBM traffic 1.30x
+  // -> 1.02x the cache bytes, 63.0 -> 57.0 us); one unit: non-temporal
+  const int64_t nwg = static_cast<int64_t>(q.num_kv_heads) * q.head_groups * q.num_seqs;
+  const size_t lds = lds_bytes<D, NWR>(q.tbl_window, 16, 0);
+  if (q.head_groups > 1) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>), dim3(static_cast<uint32_t>(nwg)),
+                       dim3(NWR * 64), lds, s, q);
+    return hipGetLastError();
+  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>), dim3(static_cast<uint32_t>(nwg)),
+                     dim3(NWR * 64), lds, s, q);
+  return hipGetLastError();
+}
+
 template <int KV, int D, int BS, int NW, bool CAUSAL>
 hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
   const int rg = p.head_groups;  // row groups of a (sequence, kv head)
@@ -1850,29 +1877,14 @@ hipError_t launch_rows(const DecodeParams &p, hipStream_t s) {
     if (e0 != hipSuccess) return e0;
   }
   if (rw_shape && static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * ((rg + 1) / 2) >= cus_rw) {
-    constexpr int NWR = 8;
     DecodeParams q = p;
     q.head_groups = (rg + 1) / 2;  // units per kv head
-    // several units per (sequence, kv head) read the same lines, side by side
-    // on one XCD: ordinary loads, so that all but the first read hit its L2
-    // (64 query heads on one kv head, 128 x 4096 tokens: HBM traffic 1.30x
-    // -> 1.02x the cache bytes, 63.0 -> 57.0 us); one unit: non-temporal
-    const int64_t nwg = static_cast<int64_t>(q.num_kv_heads) * q.head_groups * q.num_seqs;
-    const size_t lds = lds_bytes<D, NWR>(q.tbl_window, 16, 0);
-    if (q.head_groups > 1) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, false>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
-                         s, q);
-      return hipGetLastError();
-    }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_rw_kernel<KV, D, BS, NWR, CAUSAL, true>), dim3(static_cast<uint32_t>(nwg)), dim3(NWR * 64), lds,
-                       s, q);
-    return hipGetLastError();
+    // several query tokens per sequence (draft tokens): four-wavefront units,
+    // two work-groups per CU (8 draft tokens x 64/8 heads, 32 x 2048 tokens:
+    // 64.4 -> 59.4 us against eight); one token (decode, or a multi-query
+    // launch bounded to one token, which stays pa_decode bit for bit): eight
+    if (CAUSAL && p.max_q_len > 1) return launch_rw<KV, D, BS, 4, CAUSAL>(q, s);
+    return launch_rw<KV, D, BS, 8, CAUSAL>(q, s);
   }
   const int most = p.max_q_len > 1 ? NW : 2;
   // single token (also a multi-query launch bounded to one token, which is
